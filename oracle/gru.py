@@ -1,0 +1,162 @@
+"""Byte-level GRU language-model training step (oracle side; test infrastructure only).
+
+The recurrent trainer of "The Work Moved Down a Layer" (sections "The Work
+Moved Down a Layer" and "From Benchmark to Training Stages": GRU gates, the
+full cell and recurrent timesteps, RMSNorm, classifier, softmax cross-entropy,
+gradient flow, optimizer), with the recurrent state and gate math kept in FP32
+and FP16 only for GEMM inputs ("The Debugging Lesson Was Numerical").  The
+pages print no GRU equations; the cell is the standard single-layer GRU with
+gate blocks (r, z, n) along the 3H columns and the hidden bias inside the
+reset product:
+
+    GI = x_t W_i + b_i                 GH = h_{t-1} W_h + b_h
+    r  = sigmoid(GI_r + GH_r)          z  = sigmoid(GI_z + GH_z)
+    n  = tanh(GI_n + r * GH_n)         h_t = (1 - z) * n + z * h_{t-1},  h_0 = 0
+
+then RMSNorm (eps, no gain) of every h_t, the classifier Z = hn W_c + b_c,
+softmax cross-entropy against the next byte (mean over all B*T positions), full
+backpropagation through time and one momentum update over the flat buffer
+[E, W_i, b_i, W_h, b_h, W_c, b_c].
+
+Storage plan ``"f16"``: GEMM inputs (embedded x_t, the FP16 copy of h_{t-1},
+hn, dZ, the gate gradients, FP16 working copies of E and the weights) are FP16;
+GI, GH, r, z, n, h, logits, all backward carries and all gradients FP32.  The
+loss gradient dZ is stored unscaled (p - onehot), and the whole backward chain
+carries that scale; alpha = 1/(B*T) is applied where the weight, bias and
+embedding gradients are formed.  ``"f64"`` rounds nothing.  Rows of every
+[B*T x .] matrix are time-major (row = t*B + b).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import round_fmt
+from .ops import gemm_epilogue, colsum, softmax_xent, rmsnorm_fwd, rmsnorm_bwd, sgd_momentum
+
+ORDER = ("E", "W_i", "b_i", "W_h", "b_h", "W_c", "b_c")
+
+
+def _shapes(H: int, V: int):
+    return {"E": (V, H), "W_i": (H, 3 * H), "b_i": (3 * H,), "W_h": (H, 3 * H),
+            "b_h": (3 * H,), "W_c": (H, V), "b_c": (V,)}
+
+
+def gru_param_count(H: int = 1024, V: int = 256) -> int:
+    return int(sum(int(np.prod(s)) for s in _shapes(H, V).values()))
+
+
+def gru_flatten(params: dict) -> np.ndarray:
+    return np.concatenate([np.asarray(params[k], dtype=np.float64).ravel() for k in ORDER])
+
+
+def gru_unflatten(flat, H: int = 1024, V: int = 256) -> dict:
+    out, off = {}, 0
+    for k in ORDER:
+        s = _shapes(H, V)[k]
+        n = int(np.prod(s))
+        out[k] = np.asarray(flat[off:off + n]).reshape(s)
+        off += n
+    if off != len(flat):
+        raise ValueError("flat buffer size does not match H, V")
+    return out
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def gru_step(flat, vel, tokens, H: int, V: int, lr: float, momentum: float,
+             eps: float = 1e-6, plan: str = "f16", given=None, update: bool = True):
+    """One training step; returns a dict of the stored tensors, loss and update.
+
+    ``given``: optional GPU-stored tensors by name -- "hs" [T*B x H] (then the
+    recurrence at step t starts from the given h_{t-1}) -- so that per-step
+    checks do not inherit differences from earlier steps.
+    """
+    given = given or {}
+    lo = "f16" if plan == "f16" else "f64"
+    hi = "f32" if plan == "f16" else "f64"
+    P = gru_unflatten(flat, H, V)
+    Pw = {k: round_fmt(P[k], lo) for k in ("E", "W_i", "W_h", "W_c")}
+    tokens = np.asarray(tokens)
+    Bn, T1 = tokens.shape
+    T = T1 - 1
+    inp = tokens[:, :T].T.reshape(-1)            # time-major
+    tgt = tokens[:, 1:].T.reshape(-1)
+    X = Pw["E"][inp]                             # [T*B x H], FP16 values
+    GI, _ = gemm_epilogue(X, Pw["W_i"], "NN", bias=P["b_i"], out_fmt=hi)
+    hs = np.zeros((T * Bn, H))
+    hprev16 = np.zeros((T * Bn, H))
+    R = np.zeros((T * Bn, H)); Zg = np.zeros((T * Bn, H))
+    Nn = np.zeros((T * Bn, H)); GHn = np.zeros((T * Bn, H))
+    h = np.zeros((Bn, H))
+    given_hs = given.get("hs")
+    for t in range(T):
+        rows = slice(t * Bn, (t + 1) * Bn)
+        if given_hs is not None and t > 0:
+            h = np.asarray(given_hs[(t - 1) * Bn:t * Bn], dtype=np.float64)
+        h16 = round_fmt(h, lo)
+        GH, _ = gemm_epilogue(h16, Pw["W_h"], "NN", bias=P["b_h"], out_fmt=hi)
+        gi = GI[rows]
+        r = _sigmoid(gi[:, :H] + GH[:, :H])
+        z = _sigmoid(gi[:, H:2 * H] + GH[:, H:2 * H])
+        n = np.tanh(gi[:, 2 * H:] + r * GH[:, 2 * H:])
+        hn_ = (1.0 - z) * n + z * h
+        R[rows] = round_fmt(r, hi); Zg[rows] = round_fmt(z, hi); Nn[rows] = round_fmt(n, hi)
+        GHn[rows] = GH[:, 2 * H:]
+        hprev16[rows] = h16
+        h = round_fmt(hn_, hi)
+        hs[rows] = h
+    hn, rr = rmsnorm_fwd(hs, eps, y_fmt=lo, r_fmt=hi)
+    Zl, _ = gemm_epilogue(hn, Pw["W_c"], "NN", bias=P["b_c"], out_fmt=hi)
+    loss, row_loss, G, argmax = softmax_xent(Zl, tgt, 1.0, lo)
+    alpha = 1.0 / (T * Bn)
+    dW_c, _ = gemm_epilogue(hn, G, "TN", alpha, out_fmt=hi)
+    db_c = colsum(G, alpha, hi)
+    dhn, _ = gemm_epilogue(G, Pw["W_c"], "NT", out_fmt=hi)
+    dh_out, _ = rmsnorm_bwd(hs, rr, dhn, dx_fmt=hi)
+    dGH = np.zeros((T * Bn, 3 * H)); dGI = np.zeros((T * Bn, 3 * H))
+    carry = np.zeros((Bn, H))
+    for t in range(T - 1, -1, -1):
+        rows = slice(t * Bn, (t + 1) * Bn)
+        r, z, n, ghn = R[rows], Zg[rows], Nn[rows], GHn[rows]
+        hp = hs[(t - 1) * Bn:t * Bn] if t > 0 else np.zeros((Bn, H))
+        dh = dh_out[rows] + carry
+        dn = dh * (1.0 - z)
+        dz = dh * (hp - n)
+        dh_dir = round_fmt(dh * z, hi)
+        dnh = dn * (1.0 - n * n)
+        dr = dnh * ghn
+        dgr = dr * r * (1.0 - r)
+        dgz = dz * z * (1.0 - z)
+        dGH[rows] = round_fmt(np.concatenate([dgr, dgz, dnh * r], axis=1), lo)
+        dGI[rows] = round_fmt(np.concatenate([dgr, dgz, dnh], axis=1), lo)
+        carry, _ = gemm_epilogue(dGH[rows], Pw["W_h"], "NT", residual=dh_dir, out_fmt=hi)
+    dW_h, _ = gemm_epilogue(hprev16, dGH, "TN", alpha, out_fmt=hi)
+    dW_i, _ = gemm_epilogue(X, dGI, "TN", alpha, out_fmt=hi)
+    db_h = colsum(dGH, alpha, hi)
+    db_i = colsum(dGI, alpha, hi)
+    dX, _ = gemm_epilogue(dGI, Pw["W_i"], "NT", out_fmt=hi)
+    dE = np.zeros((V, H))
+    np.add.at(dE, inp, dX)
+    dE = round_fmt(alpha * dE, hi)
+    grads = {"E": dE, "W_i": dW_i, "b_i": db_i, "W_h": dW_h, "b_h": db_h,
+             "W_c": dW_c, "b_c": db_c}
+    gflat = gru_flatten(grads)
+    out = dict(loss=loss, row_loss=row_loss, GI=GI, hs=hs, R=R, Zg=Zg, N=Nn, GHn=GHn,
+               hn=hn, rstd=rr, logits=Zl, G=G, argmax=argmax, dhn=dhn, dh_out=dh_out,
+               dGH=dGH, dGI=dGI, dX=dX, grads=gflat)
+    if update:
+        if plan == "f64":
+            v2 = momentum * np.asarray(vel, dtype=np.float64) - lr * gflat
+            out.update(params=np.asarray(flat, dtype=np.float64) + v2, vel=v2, params_lowp=None)
+        else:
+            w2, v2, wl = sgd_momentum(flat, gflat, vel, lr, momentum, "f16")
+            out.update(params=w2, vel=v2, params_lowp=wl)
+    return out
+
+
+def gru_loss_only(flat, tokens, H: int, V: int, eps: float = 1e-6) -> float:
+    """Mean next-byte cross-entropy of the f64 plan (for finite differences)."""
+    return gru_step(flat, np.zeros(len(flat)), tokens, H, V, 0.0, 0.0, eps,
+                    plan="f64", update=False)["loss"]
