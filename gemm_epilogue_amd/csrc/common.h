@@ -1,0 +1,114 @@
+// Shared device/host helpers of the gfx950 GEMM-epilogue library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_epilogue.h"
+
+namespace ge {
+
+typedef _Float16 half_t;
+typedef __bf16 bf16_t;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef half_t f16x8 __attribute__((ext_vector_type(8)));
+typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
+typedef half_t f16x4 __attribute__((ext_vector_type(4)));
+typedef bf16_t bf16x4 __attribute__((ext_vector_type(4)));
+
+inline int dtype_size(int t) { return t == GE_F32 ? 4 : 2; }
+inline bool dtype_ok(int t) { return t == GE_F32 || t == GE_F16 || t == GE_BF16; }
+
+// ---- conversions (hardware conversions round to nearest even) -------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(half_t x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ half_t from_f32<half_t>(float x) { return (half_t)x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
+
+// element of a runtime-typed array
+__device__ __forceinline__ float load_any(const void *p, int64_t i, int t) {
+  if (t == GE_F32) return ((const float *)p)[i];
+  if (t == GE_F16) return (float)((const half_t *)p)[i];
+  return (float)((const bf16_t *)p)[i];
+}
+__device__ __forceinline__ void store_any(void *p, int64_t i, int t, float v) {
+  if (t == GE_F32) ((float *)p)[i] = v;
+  else if (t == GE_F16) ((half_t *)p)[i] = (half_t)v;
+  else ((bf16_t *)p)[i] = (bf16_t)v;
+}
+
+// four consecutive elements; `vec` says the address is aligned for one access
+__device__ __forceinline__ void load4_any(const void *p, int64_t i, int t, bool vec, float v[4]) {
+  if (vec) {
+    if (t == GE_F32) {
+      f32x4 x = *(const f32x4 *)((const float *)p + i);
+      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    } else if (t == GE_F16) {
+      f16x4 x = *(const f16x4 *)((const half_t *)p + i);
+      v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
+    } else {
+      bf16x4 x = *(const bf16x4 *)((const bf16_t *)p + i);
+      v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
+    }
+  } else {
+    for (int j = 0; j < 4; ++j) v[j] = load_any(p, i + j, t);
+  }
+}
+__device__ __forceinline__ void store4_any(void *p, int64_t i, int t, bool vec, const float v[4]) {
+  if (vec) {
+    if (t == GE_F32) {
+      f32x4 x = {v[0], v[1], v[2], v[3]};
+      *(f32x4 *)((float *)p + i) = x;
+    } else if (t == GE_F16) {
+      f16x4 x = {(half_t)v[0], (half_t)v[1], (half_t)v[2], (half_t)v[3]};
+      *(f16x4 *)((half_t *)p + i) = x;
+    } else {
+      bf16x4 x = {(bf16_t)v[0], (bf16_t)v[1], (bf16_t)v[2], (bf16_t)v[3]};
+      *(bf16x4 *)((bf16_t *)p + i) = x;
+    }
+  } else {
+    for (int j = 0; j < 4; ++j) store_any(p, i + j, t, v[j]);
+  }
+}
+
+// wave64 reductions (butterfly over all 64 lanes)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---- host side -------------------------------------------------------------
+void set_error(const char *fmt, ...);
+int launch_status(const char *what);  // GE_OK or GE_E_LAUNCH after hipGetLastError
+
+// aligned for a `bytes`-wide vector access at every row start
+inline bool vec_aligned(const void *p, int64_t ld, int esize, int bytes) {
+  return p != nullptr && ((uintptr_t)p % bytes) == 0 && ((ld * esize) % bytes) == 0;
+}
+
+// internal launchers (validated arguments)
+int gemm_launch(const ge_gemm_args &a, hipStream_t s);
+int64_t gemm_ws_bytes(int layout, int ab_type, int64_t M, int64_t N, int64_t K, int split_k);
+int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int x_type, float alpha,
+                  float *out, void *ws, int64_t ws_bytes, hipStream_t s);
+int64_t colsum_ws_bytes(int64_t M, int64_t N);
+int xent_launch(const float *logits, int64_t B, int64_t C, int64_t ld, const int32_t *labels,
+                float grad_scale, float *loss_mean, float *row_loss, void *dl, int64_t ld_d,
+                int d_type, int32_t *argmax, hipStream_t s);
+int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t s);
+int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D);
+int sgd_launch(float *w, const float *g, float *v, float lr, float mu, int64_t n, void *wl,
+               int lt, hipStream_t s);
+
+}  // namespace ge

@@ -1,0 +1,395 @@
+// Bandwidth-bound kernels of the training step, for gfx950 (wave64):
+// column sums (bias gradients), stable softmax cross-entropy, RMSNorm forward
+// and backward, and the flat SGD-momentum update.
+//
+// All reductions run in FP32 in a fixed order (per-lane sequential sums, then
+// a fixed butterfly across the 64 lanes, then a fixed order across waves and
+// blocks), so results are bitwise reproducible ("The Work Moved Down a Layer",
+// section "The Debugging Lesson Was Numerical": reductions for softmax and
+// loss in FP32).  Loads and stores are 16-byte (FP32) or 8-byte (16-bit)
+// vectors of four consecutive elements wherever alignment allows.
+#include <algorithm>
+
+#include "common.h"
+
+namespace ge {
+
+// =========================== column sums ====================================
+// "Capstone 5: train a network with your CUDA kernels", section "Work through
+// the backward pass": db = sum_rows(dZ), a reduction across the batch.
+//
+// A block of 256 threads owns 256 consecutive columns (four per lane) and a
+// contiguous range of rows; wave w sums rows w, w+4, w+8, ... of the range in
+// order, then the four wave partials are added in wave order.  With several
+// row ranges the partials go to a workspace and colsum_final adds them in
+// range order.
+constexpr int CS_COLS = 256;
+constexpr int CS_ROWS_MIN = 64;
+
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const void *__restrict__ X, int M, int N,
+                                                             int64_t ldx, int xt, int vec, int rows_per,
+                                                             float alpha, float *__restrict__ out) {
+  __shared__ float red[4][CS_COLS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * CS_COLS + lane * 4;
+  const int r0 = blockIdx.y * rows_per;
+  const int r1 = min(M, r0 + rows_per);
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  if (n < N) {
+    const bool full = n + 3 < N;
+    for (int r = r0 + wave; r < r1; r += 4) {
+      float v[4];
+      if (full) {
+        load4_any(X, (int64_t)r * ldx + n, xt, vec, v);
+      } else {
+        for (int j = 0; j < 4; ++j) v[j] = (n + j < N) ? load_any(X, (int64_t)r * ldx + n + j, xt) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] += v[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[wave][lane * 4 + j] = s[j];
+  __syncthreads();
+  if (wave == 0 && n < N) {
+    float *dst = out + (int64_t)blockIdx.y * N;
+    for (int j = 0; j < 4; ++j) {
+      const int c = lane * 4 + j;
+      const float t = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+      if (n + j < N) dst[n + j] = alpha * t;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restrict__ part, int splits, int N,
+                                                           float alpha, float *__restrict__ out) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * N + n];
+  out[n] = alpha * s;
+}
+
+namespace {
+int colsum_splits(int64_t M, int64_t N) {
+  if (M < 1024) return 1;  // one pass: a block reads all rows of its columns
+  const int64_t colblocks = (N + CS_COLS - 1) / CS_COLS;
+  int64_t want = (1024 + colblocks - 1) / colblocks;
+  int64_t maxs = std::max<int64_t>(1, M / CS_ROWS_MIN);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(maxs, 1024)));
+}
+}  // namespace
+
+int64_t colsum_ws_bytes(int64_t M, int64_t N) {
+  if (M <= 0 || N <= 0) return 0;
+  const int s = colsum_splits(M, N);
+  return s > 1 ? (int64_t)s * N * 4 : 0;
+}
+
+int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt, float alpha, float *out,
+                  void *ws, int64_t ws_bytes, hipStream_t st) {
+  if (N == 0) return GE_OK;
+  const int vec = vec_aligned(X, ldx, dtype_size(xt), 4 * dtype_size(xt));
+  const int colblocks = (int)((N + CS_COLS - 1) / CS_COLS);
+  const int splits = M > 0 ? colsum_splits(M, N) : 1;
+  if (splits == 1) {
+    hipLaunchKernelGGL(colsum_partial_kernel, dim3(colblocks, 1), dim3(256), 0, st, X, (int)M, (int)N, ldx,
+                       xt, vec, (int)std::max<int64_t>(M, 1), alpha, out);
+    return launch_status("colsum");
+  }
+  const int64_t need = (int64_t)splits * N * 4;
+  if (ws == nullptr || ws_bytes < need) {
+    set_error("colsum: %lld rows need %lld workspace bytes", (long long)M, (long long)need);
+    return GE_E_WORKSPACE;
+  }
+  const int rows_per = (int)((M + splits - 1) / splits);
+  hipLaunchKernelGGL(colsum_partial_kernel, dim3(colblocks, splits), dim3(256), 0, st, X, (int)M, (int)N,
+                     ldx, xt, vec, rows_per, 1.0f, (float *)ws);
+  int s = launch_status("colsum (partial)");
+  if (s != GE_OK) return s;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
+                     (const float *)ws, splits, (int)N, alpha, out);
+  return launch_status("colsum (final)");
+}
+
+// ====================== softmax cross-entropy ===============================
+// "Capstone 5", sections "The minimum model" and "Read the worked reference":
+// stable softmax cross-entropy -- subtract the row maximum before exp -- gives
+// the loss and dZ.  One wavefront per row; lanes stride the classes.
+__global__ __launch_bounds__(256) void xent_rows_kernel(const float *__restrict__ Z, int B, int C, int64_t ld,
+                                                        const int32_t *__restrict__ labels, float gscale,
+                                                        float *__restrict__ row_loss, void *__restrict__ dZ,
+                                                        int64_t ldd, int dt, int32_t *__restrict__ amax) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= B) return;
+  const float *z = Z + (int64_t)row * ld;
+  // max and lowest index of the max
+  float m = -INFINITY;
+  int mi = 0x7fffffff;
+  for (int c = lane; c < C; c += 64) {
+    const float v = z[c];
+    if (v > m) { m = v; mi = c; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, 64);
+    const int oi = __shfl_xor(mi, o, 64);
+    if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+  }
+  float s = 0.f;
+  for (int c = lane; c < C; c += 64) s += expf(z[c] - m);
+  s = wave_sum(s);
+  const float lse = m + logf(s);
+  const int y = labels[row];
+  if (lane == 0) {
+    // a label outside [0, C) reads nothing and yields a NaN row loss
+    row_loss[row] = ((unsigned)y < (unsigned)C) ? lse - z[y] : NAN;
+    if (amax) amax[row] = mi;
+  }
+  if (dZ) {
+    for (int c = lane; c < C; c += 64) {
+      const float p = expf(z[c] - lse);
+      store_any(dZ, (int64_t)row * ldd + c, dt, gscale * (p - (c == y ? 1.f : 0.f)));
+    }
+  }
+}
+
+// mean of the row losses: one block, fixed order (thread t sums rows t, t+256,
+// ..., then a fixed tree over the 256 partials).
+__global__ __launch_bounds__(256) void xent_mean_kernel(const float *__restrict__ row_loss, int B,
+                                                        float *__restrict__ out) {
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < B; i += 256) s += row_loss[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = B > 0 ? red[0] / (float)B : 0.f;
+}
+
+int xent_launch(const float *Z, int64_t B, int64_t C, int64_t ld, const int32_t *labels, float gscale,
+                float *loss_mean, float *row_loss, void *dZ, int64_t ldd, int dt, int32_t *amax,
+                hipStream_t st) {
+  if (B > 0) {
+    hipLaunchKernelGGL(xent_rows_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, Z, (int)B, (int)C,
+                       ld, labels, gscale, row_loss, dZ, ldd, dt, amax);
+    int s = launch_status("softmax_xent_fwd_bwd (rows)");
+    if (s != GE_OK) return s;
+  }
+  hipLaunchKernelGGL(xent_mean_kernel, dim3(1), dim3(256), 0, st, row_loss, (int)B, loss_mean);
+  return launch_status("softmax_xent_fwd_bwd (mean)");
+}
+
+// ============================== RMSNorm =====================================
+// FP32 statistics ("The Work Moved Down a Layer", "The Debugging Lesson Was
+// Numerical"); the block's first step ("Full-Depth MLP Megakernel ...", "What
+// Worked").  One wavefront per row; the row lives in registers (CH chunks of
+// four elements per lane, D <= 256*CH).
+template <int CH>
+__global__ __launch_bounds__(256) void rms_fwd_kernel(ge_rmsnorm_args a, int vx, int vy) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int D = (int)a.D;
+  float x[CH][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j = (c * 64 + lane) * 4;
+    if (j + 3 < D) {
+      load4_any(a.x, row * a.ld_x + j, a.x_type, vx, x[c]);
+    } else {
+      for (int e = 0; e < 4; ++e) x[c][e] = (j + e < D) ? load_any(a.x, row * a.ld_x + j + e, a.x_type) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += x[c][e] * x[c][e];
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+  if (lane == 0) a.r[row] = r;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j = (c * 64 + lane) * 4;
+    if (j >= D) continue;
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = x[c][e] * r * (a.gamma && j + e < D ? a.gamma[j + e] : 1.f);
+    if (j + 3 < D) {
+      store4_any(a.y, row * a.ld_y + j, a.y_type, vy, y);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (j + e < D) store_any(a.y, row * a.ld_y + j + e, a.y_type, y[e]);
+    }
+  }
+}
+
+// dx = r * (g - xh * mean(g * xh)) + dres,  xh = x * r,  g = dy * gamma.
+// With dgamma requested, each block also writes its partial sum_rows dy * xh
+// for its 4 rows into the workspace ([blocks x D], block order).
+template <int CH>
+__global__ __launch_bounds__(256) void rms_bwd_kernel(ge_rmsnorm_args a, int vx, int vdy, int vres, int vdx,
+                                                      float *__restrict__ dg_part) {
+  __shared__ float dgs[4][256 * CH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  const bool live = row < a.rows;
+  const int D = (int)a.D;
+  float xh[CH][4], g[CH][4];
+  float dot = 0.f;
+  const float r = live ? a.r[row] : 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j = (c * 64 + lane) * 4;
+    float xv[4], dv[4];
+    if (live && j + 3 < D) {
+      load4_any(a.x, row * a.ld_x + j, a.x_type, vx, xv);
+      load4_any(a.dy, row * a.ld_dy + j, a.dy_type, vdy, dv);
+    } else {
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = live && j + e < D;
+        xv[e] = ok ? load_any(a.x, row * a.ld_x + j + e, a.x_type) : 0.f;
+        dv[e] = ok ? load_any(a.dy, row * a.ld_dy + j + e, a.dy_type) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xh[c][e] = xv[e] * r;
+      g[c][e] = dv[e] * ((a.gamma && j + e < D) ? a.gamma[j + e] : 1.f);
+      dot += g[c][e] * xh[c][e];
+      if (dg_part) dgs[wave][c * 256 + lane * 4 + e] = dv[e] * xh[c][e];
+    }
+  }
+  dot = wave_sum(dot);
+  const float cm = dot / (float)D;
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int j = (c * 64 + lane) * 4;
+      if (j >= D) continue;
+      float dx[4], rs[4] = {0.f, 0.f, 0.f, 0.f};
+      if (a.dres) {
+        if (j + 3 < D) load4_any(a.dres, row * a.ld_dres + j, a.dres_type, vres, rs);
+        else
+          for (int e = 0; e < 4; ++e) rs[e] = (j + e < D) ? load_any(a.dres, row * a.ld_dres + j + e, a.dres_type) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dx[e] = r * (g[c][e] - xh[c][e] * cm) + rs[e];
+      if (j + 3 < D) {
+        store4_any(a.dx, row * a.ld_dx + j, a.dx_type, vdx, dx);
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (j + e < D) store_any(a.dx, row * a.ld_dx + j + e, a.dx_type, dx[e]);
+      }
+    }
+  }
+  if (dg_part) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < D; i += 256) {
+      // column i of chunk layout: chunk c = i / 256, lane*4+e = i % 256
+      const int c = i / 256, o = i % 256;
+      const float t = ((dgs[0][c * 256 + o] + dgs[1][c * 256 + o]) + dgs[2][c * 256 + o]) + dgs[3][c * 256 + o];
+      dg_part[(int64_t)blockIdx.x * D + i] = t;
+    }
+  }
+}
+
+// dgamma[j] = sum over blocks of the partials, in block order
+__global__ __launch_bounds__(256) void rms_dgamma_final(const float *__restrict__ part, int nb, int D,
+                                                        float *__restrict__ dgamma) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= D) return;
+  float s = 0.f;
+  for (int b = 0; b < nb; ++b) s += part[(int64_t)b * D + j];
+  dgamma[j] = s;
+}
+
+int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D) { return ((rows + 3) / 4) * D * 4; }
+
+namespace {
+template <int CH> int rms_dispatch(const ge_rmsnorm_args &a, hipStream_t st) {
+  const unsigned blocks = (unsigned)((a.rows + 3) / 4);
+  auto al = [](const void *p, int64_t ld, int t) { return p ? (int)vec_aligned(p, ld, dtype_size(t), 4 * dtype_size(t)) : 0; };
+  if (a.pass == GE_FWD) {
+    hipLaunchKernelGGL(rms_fwd_kernel<CH>, dim3(blocks), dim3(256), 0, st, a, al(a.x, a.ld_x, a.x_type),
+                       al(a.y, a.ld_y, a.y_type));
+    return launch_status("rmsnorm_fwd_bwd (fwd)");
+  }
+  float *part = nullptr;
+  if (a.dgamma) {
+    if (a.workspace == nullptr || a.workspace_bytes < rmsnorm_ws_bytes(a.rows, a.D)) {
+      set_error("rmsnorm_fwd_bwd: dgamma needs %lld workspace bytes", (long long)rmsnorm_ws_bytes(a.rows, a.D));
+      return GE_E_WORKSPACE;
+    }
+    part = (float *)a.workspace;
+  }
+  hipLaunchKernelGGL(rms_bwd_kernel<CH>, dim3(blocks), dim3(256), 0, st, a, al(a.x, a.ld_x, a.x_type),
+                     al(a.dy, a.ld_dy, a.dy_type), al(a.dres, a.ld_dres, a.dres_type),
+                     al(a.dx, a.ld_dx, a.dx_type), part);
+  int s = launch_status("rmsnorm_fwd_bwd (bwd)");
+  if (s != GE_OK || !a.dgamma) return s;
+  hipLaunchKernelGGL(rms_dgamma_final, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, st,
+                     (const float *)part, (int)blocks, (int)a.D, a.dgamma);
+  return launch_status("rmsnorm_fwd_bwd (dgamma)");
+}
+}  // namespace
+
+int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t st) {
+  if (a.rows == 0) return GE_OK;
+  if (a.D <= 256) return rms_dispatch<1>(a, st);
+  if (a.D <= 512) return rms_dispatch<2>(a, st);
+  if (a.D <= 1024) return rms_dispatch<4>(a, st);
+  if (a.D <= 2048) return rms_dispatch<8>(a, st);
+  return rms_dispatch<16>(a, st);
+}
+
+// =========================== SGD momentum ===================================
+// "Capstone 5", section "Read the worked reference": one grid-stride update
+// over the flat parameter buffer: vel = mu * v - lr * g; v = vel; w += vel.
+// Four elements per thread per iteration (16-byte accesses).
+__global__ __launch_bounds__(256) void sgd_kernel(float *__restrict__ w, const float *__restrict__ g,
+                                                  float *__restrict__ v, float lr, float mu, int64_t n,
+                                                  void *__restrict__ wl, int lt, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (vec && i + 3 < n) {
+      f32x4 wv = *(f32x4 *)(w + i);
+      const f32x4 gv = *(const f32x4 *)(g + i);
+      f32x4 vv = *(f32x4 *)(v + i);
+      float out[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float vel = mu * vv[e] - lr * gv[e];
+        vv[e] = vel;
+        wv[e] = wv[e] + vel;
+        out[e] = wv[e];
+      }
+      *(f32x4 *)(v + i) = vv;
+      *(f32x4 *)(w + i) = wv;
+      if (wl) store4_any(wl, i, lt, true, out);
+    } else {
+      for (int64_t k = i; k < n && k < i + 4; ++k) {
+        const float vel = mu * v[k] - lr * g[k];
+        v[k] = vel;
+        w[k] = w[k] + vel;
+        if (wl) store_any(wl, k, lt, w[k]);
+      }
+    }
+  }
+}
+
+int sgd_launch(float *w, const float *g, float *v, float lr, float mu, int64_t n, void *wl, int lt,
+               hipStream_t st) {
+  if (n == 0) return GE_OK;
+  const int vec = ((uintptr_t)w % 16 == 0) && ((uintptr_t)g % 16 == 0) && ((uintptr_t)v % 16 == 0) &&
+                  (wl == nullptr || (uintptr_t)wl % 8 == 0);
+  const int64_t items = (n + 3) / 4;
+  const unsigned blocks = (unsigned)std::min<int64_t>((items + 255) / 256, 2048);
+  hipLaunchKernelGGL(sgd_kernel, dim3(blocks), dim3(256), 0, st, w, g, v, lr, mu, n, wl, lt, vec);
+  return launch_status("sgd_momentum");
+}
+
+}  // namespace ge

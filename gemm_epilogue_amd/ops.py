@@ -1,0 +1,237 @@
+"""torch-tensor wrappers over the C ABI: argument marshalling only.
+
+Every computation runs in libgemm_epilogue.so on the caller's current HIP
+stream.  torch is used for device memory (outputs and workspaces allocated
+here when the caller passes none) and for the stream handle.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from ._lib import (ACT, GE_BF16, GE_BWD, GE_F16, GE_F32, GE_FWD, LAYOUT, GemmArgs,
+                   MlpBuffers, MlpDesc, RmsnormArgs, check, lib)
+
+_DT = {torch.float32: GE_F32, torch.float16: GE_F16, torch.bfloat16: GE_BF16}
+_TD = {v: k for k, v in _DT.items()}
+
+
+def dtype_code(t: torch.dtype) -> int:
+    try:
+        return _DT[t]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t}") from None
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a row-major 2-D tensor (unit column stride)")
+    return max(t.stride(0), t.shape[1], 1)
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes <= 0:
+        return ws
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gemm_shape(A, B, layout: str):
+    if layout == "NN":
+        return A.shape[0], B.shape[1], A.shape[1]
+    if layout == "NT":
+        return A.shape[0], B.shape[0], A.shape[1]
+    if layout == "TN":
+        return A.shape[1], B.shape[1], A.shape[0]
+    raise ValueError(layout)
+
+
+def gemm_workspace_bytes(layout: str, dtype, M, N, K, split_k=0) -> int:
+    return int(lib.gemm_workspace_bytes(LAYOUT[layout], dtype_code(dtype), M, N, K, split_k))
+
+
+def gemm_bias_act(A, B, layout: str = "NN", *, out=None, out_dtype=torch.float32, alpha=1.0,
+                  bias=None, act: str = "none", slope: float = 0.5, aux=None, residual=None,
+                  pre=None, workspace=None, split_k: int = 0):
+    """C = act(alpha * op(A) op(B) + bias) [+ residual]  (see gemm_bias_act in the header)."""
+    M, N, K = gemm_shape(A, B, layout)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    ws_need = gemm_workspace_bytes(layout, A.dtype, M, N, K, split_k)
+    ws = _workspace(ws_need, A.device, workspace)
+    a = GemmArgs()
+    a.layout = LAYOUT[layout]
+    a.ab_type = dtype_code(A.dtype)
+    a.M, a.N, a.K = M, N, K
+    a.A, a.lda = A.data_ptr(), _ld(A)
+    a.B, a.ldb = B.data_ptr(), _ld(B)
+    a.alpha = alpha
+    a.bias = None if bias is None else bias.data_ptr()
+    a.act = ACT[act]
+    a.act_slope = slope
+    if aux is not None:
+        a.aux, a.ld_aux, a.aux_type = aux.data_ptr(), _ld(aux), dtype_code(aux.dtype)
+    if residual is not None:
+        a.residual, a.ld_res, a.res_type = residual.data_ptr(), _ld(residual), dtype_code(residual.dtype)
+    a.C, a.ldc, a.c_type = out.data_ptr(), _ld(out), dtype_code(out.dtype)
+    if pre is not None:
+        a.pre, a.ld_pre, a.pre_type = pre.data_ptr(), _ld(pre), dtype_code(pre.dtype)
+    if ws is not None:
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    a.split_k = split_k
+    check(lib.gemm_bias_act(C.byref(a), _stream()), "gemm_bias_act")
+    return out
+
+
+def colsum(X, alpha: float = 1.0, *, out=None, workspace=None):
+    """out[n] = alpha * sum_m X[m, n]  (f32)."""
+    M, N = X.shape
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=X.device)
+    ws = _workspace(int(lib.colsum_workspace_bytes(M, N)), X.device, workspace)
+    check(lib.colsum(_ptr(X), M, N, _ld(X), dtype_code(X.dtype), alpha, _ptr(out), _ptr(ws),
+                     0 if ws is None else ws.numel() * ws.element_size(), _stream()), "colsum")
+    return out
+
+
+def softmax_xent_fwd_bwd(logits, labels, grad_scale: float, *, d_dtype=torch.float32,
+                         want_grad=True, want_argmax=True, loss=None, row_loss=None, dlogits=None,
+                         argmax=None):
+    """Returns (loss_mean[1], row_loss[B], dlogits or None, argmax or None)."""
+    B, Cn = logits.shape
+    dev = logits.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    row_loss = torch.empty(B, dtype=torch.float32, device=dev) if row_loss is None else row_loss
+    if want_grad and dlogits is None:
+        dlogits = torch.empty((B, Cn), dtype=d_dtype, device=dev)
+    if want_argmax and argmax is None:
+        argmax = torch.empty(B, dtype=torch.int32, device=dev)
+    check(lib.softmax_xent_fwd_bwd(
+        _ptr(logits), B, Cn, _ld(logits), _ptr(labels), grad_scale, _ptr(loss), _ptr(row_loss),
+        _ptr(dlogits), 0 if dlogits is None else _ld(dlogits),
+        GE_F32 if dlogits is None else dtype_code(dlogits.dtype), _ptr(argmax), _stream()),
+        "softmax_xent_fwd_bwd")
+    return loss, row_loss, dlogits, argmax
+
+
+def rmsnorm_fwd(x, eps: float, *, y_dtype=None, gamma=None, y=None, r=None):
+    """Returns (y, r) with r = 1/sqrt(mean x^2 + eps) per row (f32)."""
+    rows, D = x.shape
+    y = torch.empty((rows, D), dtype=y_dtype or x.dtype, device=x.device) if y is None else y
+    r = torch.empty(rows, dtype=torch.float32, device=x.device) if r is None else r
+    a = RmsnormArgs()
+    a.pass_, a.rows, a.D, a.eps = GE_FWD, rows, D, eps
+    a.x, a.ld_x, a.x_type = x.data_ptr(), _ld(x), dtype_code(x.dtype)
+    a.gamma = None if gamma is None else gamma.data_ptr()
+    a.y, a.ld_y, a.y_type = y.data_ptr(), _ld(y), dtype_code(y.dtype)
+    a.r = r.data_ptr()
+    check(lib.rmsnorm_fwd_bwd(C.byref(a), _stream()), "rmsnorm_fwd_bwd(fwd)")
+    return y, r
+
+
+def rmsnorm_bwd(x, r, dy, *, dres=None, gamma=None, dx_dtype=None, dx=None, dgamma=None,
+                workspace=None):
+    """Returns (dx, dgamma or None)."""
+    rows, D = x.shape
+    dx = torch.empty((rows, D), dtype=dx_dtype or x.dtype, device=x.device) if dx is None else dx
+    a = RmsnormArgs()
+    a.pass_, a.rows, a.D = GE_BWD, rows, D
+    a.x, a.ld_x, a.x_type = x.data_ptr(), _ld(x), dtype_code(x.dtype)
+    a.gamma = None if gamma is None else gamma.data_ptr()
+    a.r = r.data_ptr()
+    a.dy, a.ld_dy, a.dy_type = dy.data_ptr(), _ld(dy), dtype_code(dy.dtype)
+    if dres is not None:
+        a.dres, a.ld_dres, a.dres_type = dres.data_ptr(), _ld(dres), dtype_code(dres.dtype)
+    a.dx, a.ld_dx, a.dx_type = dx.data_ptr(), _ld(dx), dtype_code(dx.dtype)
+    if dgamma is not None:
+        ws = _workspace(int(lib.rmsnorm_workspace_bytes(rows, D)), x.device, workspace)
+        a.dgamma = dgamma.data_ptr()
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    check(lib.rmsnorm_fwd_bwd(C.byref(a), _stream()), "rmsnorm_fwd_bwd(bwd)")
+    return dx, dgamma
+
+
+def sgd_momentum(w, g, v, lr: float, momentum: float, w_lowp=None):
+    """In place: v = momentum*v - lr*g; w += v; w_lowp = convert(w)."""
+    lt = GE_F16 if w_lowp is None else dtype_code(w_lowp.dtype)
+    check(lib.sgd_momentum(_ptr(w), _ptr(g), _ptr(v), lr, momentum, w.numel(), _ptr(w_lowp), lt,
+                           _stream()), "sgd_momentum")
+
+
+# ------------------------------------------------------------------ MLP ------
+
+def mlp_param_count(dims) -> int:
+    arr = (C.c_int64 * len(dims))(*dims)
+    return int(lib.mlp_param_count(len(dims) - 1, arr))
+
+
+class MLPTrainer:
+    """Device buffers of one dense ReLU MLP and a call of mlp_train_step per step.
+
+    params / velocity are f32 flat buffers [W1, b1, W2, b2, ...]; with FP16
+    storage an FP16 working copy of the parameters is kept beside them.
+    """
+
+    def __init__(self, dims, batch: int, storage=torch.float32, device="cuda", params=None):
+        self.dims = list(dims)
+        self.batch = batch
+        self.storage = storage
+        self._dims_c = (C.c_int64 * len(dims))(*dims)
+        self.desc = MlpDesc(len(dims) - 1, self._dims_c, dtype_code(storage))
+        P = mlp_param_count(dims)
+        self.P = P
+        self.params = torch.zeros(P, dtype=torch.float32, device=device)
+        if params is not None:
+            self.params.copy_(params)
+        self.grads = torch.zeros(P, dtype=torch.float32, device=device)
+        self.velocity = torch.zeros(P, dtype=torch.float32, device=device)
+        self.params_lowp = (self.params.to(torch.float16) if storage == torch.float16 else None)
+        nbytes = int(lib.mlp_workspace_bytes(C.byref(self.desc), batch))
+        check(0 if nbytes >= 0 else -1, "mlp_workspace_bytes")
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self.bufs = MlpBuffers(self.params.data_ptr(), self.grads.data_ptr(),
+                               self.velocity.data_ptr(),
+                               None if self.params_lowp is None else self.params_lowp.data_ptr(),
+                               self.workspace.data_ptr(), self.workspace.numel())
+
+    def sync_lowp(self):
+        if self.params_lowp is not None:
+            self.params_lowp.copy_(self.params.to(torch.float16))
+
+    def step(self, X, labels, lr: float, momentum: float, batch=None):
+        B = X.shape[0] if batch is None else batch
+        if B > self.batch:
+            raise ValueError("batch larger than the workspace was sized for")
+        check(lib.mlp_train_step(C.byref(self.desc), C.byref(self.bufs), _ptr(X), _ptr(labels), B,
+                                 lr, momentum, _ptr(self.loss), _stream()), "mlp_train_step")
+        return self.loss
+
+    def workspace_views(self, B=None):
+        """Views of the stored activations H_1..H_{L-1}, logits Z, dZ and row losses."""
+        B = self.batch if B is None else B
+        L = len(self.dims) - 1
+        offs = (C.c_int64 * (L + 2))()
+        check(lib.mlp_workspace_offsets(C.byref(self.desc), B, offs, L + 2), "mlp_workspace_offsets")
+        ws = self.workspace
+        out = {"H": []}
+        for l in range(1, L):
+            n = B * self.dims[l]
+            es = 2 if self.storage == torch.float16 else 4
+            out["H"].append(ws[offs[l - 1]:offs[l - 1] + n * es].view(self.storage).view(B, self.dims[l]))
+        Cn = self.dims[-1]
+        out["Z"] = ws[offs[L - 1]:offs[L - 1] + B * Cn * 4].view(torch.float32).view(B, Cn)
+        es = 2 if self.storage == torch.float16 else 4
+        out["G"] = ws[offs[L]:offs[L] + B * Cn * es].view(self.storage).view(B, Cn)
+        out["row_loss"] = ws[offs[L + 1]:offs[L + 1] + B * 4].view(torch.float32)
+        return out

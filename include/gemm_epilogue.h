@@ -1,0 +1,269 @@
+/*
+ * gemm_epilogue.h -- C ABI of the MI355X (gfx950) GEMM-epilogue training path.
+ *
+ * One training step of a small dense network: mixed-precision GEMMs (FP16 /
+ * BF16 / FP32 inputs, FP32 accumulation on MFMA) whose bias and activation are
+ * applied to the FP32 accumulator in the epilogue, converted once at the final
+ * store, plus the glue around them: stable softmax cross-entropy forward and
+ * backward, RMSNorm with FP32 statistics, column-sum bias gradients, the
+ * ReLU-mask backward (a dgrad-GEMM epilogue) and one flat SGD-momentum update.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Memory: the caller allocates and owns all device memory (inputs,
+ *    outputs, parameters, gradients, velocity, workspace).  The library never
+ *    allocates or frees device memory and never synchronises; pointers named
+ *    "device" must point to device memory (or be NULL where allowed).  Host
+ *    structs passed by pointer are read during the call only.
+ *  - Streams: every call enqueues asynchronously on `stream` (a hipStream_t;
+ *    NULL = the null stream) and returns before the work finishes.
+ *  - Layout: all matrices are row-major with an explicit leading dimension
+ *    (elements between consecutive rows, >= the row length).
+ *  - Errors: every call returns GE_OK or a negative status.  Arguments are
+ *    validated on the host before anything is enqueued; on GE_E_INVALID,
+ *    GE_E_UNSUPPORTED or GE_E_WORKSPACE nothing was enqueued.  GE_E_LAUNCH
+ *    reports a HIP launch error.  ge_last_error() returns a thread-local
+ *    message for the last failing call.  No call aborts or prints.
+ *  - Determinism: for identical inputs the results are bitwise identical from
+ *    run to run (no floating-point atomics; split-K partials and every
+ *    reduction are summed in a fixed order).
+ *
+ * Sources (web pages; cited by title and section):
+ *  [CAP] "Capstone 5: train a network with your CUDA kernels" (Day 100).
+ *  [CAT] "The Work Moved Down a Layer" (Cat Chat, Vulkan compute).
+ *  [MK]  "Full-Depth MLP Megakernel + Fused Attention Preprocessing".
+ */
+#ifndef GEMM_EPILOGUE_H
+#define GEMM_EPILOGUE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ge_stream_t; /* hipStream_t */
+
+/* status codes */
+#define GE_OK 0
+#define GE_E_INVALID (-1)     /* bad argument; nothing enqueued */
+#define GE_E_UNSUPPORTED (-2) /* valid but not supported combination */
+#define GE_E_LAUNCH (-3)      /* HIP launch error */
+#define GE_E_WORKSPACE (-4)   /* workspace missing or too small */
+
+/* storage types */
+#define GE_F32 0
+#define GE_F16 1  /* IEEE binary16 */
+#define GE_BF16 2 /* bfloat16 */
+
+/* operand layouts (see gemm_bias_act) */
+#define GE_NN 0
+#define GE_NT 1
+#define GE_TN 2
+
+/* epilogue activations */
+#define GE_ACT_NONE 0
+#define GE_ACT_RELU 1          /* max(v, 0)                      [CAP] Read the worked reference */
+#define GE_ACT_LRELU_SQ 2      /* (v > 0 ? v : s*v)^2            [MK] What Worked */
+#define GE_ACT_RELU_MASK_BWD 3 /* v * [aux > 0]                  [CAP] Work through the backward pass */
+#define GE_ACT_LRELU_SQ_BWD 4  /* v * (aux > 0 ? 2aux : 2s^2 aux) [MK] Credits (backward epilogue) */
+
+int ge_abi_version(void); /* returns 1 */
+const char *ge_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * gemm_bias_act -- C = act(alpha * op(A) op(B) + bias) [+ residual]
+ *
+ * [CAP] "Read the worked reference": the forward multiply keeps bias and ReLU
+ * in its epilogue; "Work through the backward pass": dW = X^T dH and
+ * dX = dH W^T are multiplies with one transposed input, dH applies the ReLU
+ * mask.  [CAT] "The Debugging Lesson Was Numerical": accumulate in FP32, apply
+ * bias and activation in FP32, convert once at the final store.
+ *
+ * Layouts (row-major storage):
+ *   GE_NN: A [M x K] (lda >= K), B [K x N] (ldb >= N):  C = A   B
+ *   GE_NT: A [M x K] (lda >= K), B [N x K] (ldb >= K):  C = A   B^T
+ *   GE_TN: A [K x M] (lda >= M), B [K x N] (ldb >= N):  C = A^T B
+ * A and B share ab_type (F32, F16 or BF16); products accumulate in FP32.
+ * Epilogue, per element (m, n), all in FP32:
+ *   v = alpha * acc + (bias ? bias[n] : 0)          bias: device f32 [N] or NULL
+ *   pre[m, n] = convert(v)                          optional pre-activation store
+ *   forward acts (NONE, RELU, LRELU_SQ): v = act(v)
+ *   backward acts (*_BWD): v = v * f(aux[m, n])     aux required, aux_type, ld_aux
+ *   v += residual[m, n]                             optional (res_type, ld_res)
+ *   C[m, n] = convert(v)                            c_type, ldc; one RNE rounding
+ * act_slope is the leaky slope s of the LRELU_SQ pair (0.5 in the MLP block).
+ * M, N, K >= 0 (M or N == 0: no-op; K == 0: acc = 0).  C must not alias A, B.
+ * Split-K: large-K, small-output problems split the K loop; FP32 partials go
+ * to `workspace` and are summed in fixed order by a finishing pass that
+ * applies the epilogue.  gemm_workspace_bytes() gives the size needed
+ * (0 if none); split_k = 0 picks automatically, >= 1 forces that count.
+ * ---------------------------------------------------------------------- */
+typedef struct ge_gemm_args {
+  int32_t layout;  /* GE_NN / GE_NT / GE_TN */
+  int32_t ab_type; /* GE_F32 / GE_F16 / GE_BF16 */
+  int64_t M, N, K;
+  const void *A; /* device */
+  int64_t lda;
+  const void *B; /* device */
+  int64_t ldb;
+  float alpha;
+  const float *bias; /* device f32 [N] or NULL */
+  int32_t act;       /* GE_ACT_* */
+  float act_slope;
+  const void *aux; /* device [M x N] or NULL (required by *_BWD acts) */
+  int64_t ld_aux;
+  int32_t aux_type;
+  const void *residual; /* device [M x N] or NULL */
+  int64_t ld_res;
+  int32_t res_type;
+  void *C; /* device [M x N] */
+  int64_t ldc;
+  int32_t c_type;
+  void *pre; /* device [M x N] or NULL */
+  int64_t ld_pre;
+  int32_t pre_type;
+  void *workspace; /* device or NULL */
+  int64_t workspace_bytes;
+  int32_t split_k; /* 0 = auto */
+} ge_gemm_args;
+
+int gemm_bias_act(const ge_gemm_args *args, ge_stream_t stream);
+/* bytes of workspace gemm_bias_act needs for this problem with split_k
+ * (0 = the automatic choice); 0 when no split is used. */
+int64_t gemm_workspace_bytes(int32_t layout, int32_t ab_type, int64_t M, int64_t N,
+                             int64_t K, int32_t split_k);
+
+/* ------------------------------------------------------------------------
+ * colsum -- out[n] = alpha * sum_m X[m, n]   (bias gradients)
+ * [CAP] "Work through the backward pass" / "Check your mapping": each db is
+ * a column reduction over the batch.  X: device [M x N] (x_type, ldx >= N);
+ * out: device f32 [N].  Sums in FP32 in a fixed order.  Problems with many
+ * rows use a two-pass reduction whose partials live in `workspace`
+ * (colsum_workspace_bytes(M, N) bytes; 0 means none needed).
+ * ---------------------------------------------------------------------- */
+int colsum(const void *X, int64_t M, int64_t N, int64_t ldx, int32_t x_type, float alpha,
+           float *out, void *workspace, int64_t workspace_bytes, ge_stream_t stream);
+int64_t colsum_workspace_bytes(int64_t M, int64_t N);
+
+/* ------------------------------------------------------------------------
+ * softmax_xent_fwd_bwd -- stable softmax cross-entropy, loss and dlogits
+ * [CAP] "The minimum model" and "Read the worked reference": subtract each
+ * row's maximum before exponentiating; the loss kernel yields loss and dZ.
+ * [CAT] "The Debugging Lesson Was Numerical": reductions in FP32.
+ *   per row b:  m = max_c z;  lse = m + log(sum_c exp(z - m));
+ *               row_loss[b] = lse - z[label[b]];
+ *               dlogits[b, c] = grad_scale * (exp(z - lse) - [c == label[b]])
+ *   loss_mean[0] = (1/B) sum_b row_loss[b]      (fixed-order sum)
+ *   argmax[b] = lowest index of the row maximum  (optional)
+ * logits: device f32 [B x C] (ld >= C); labels: device int32 [B] in [0, C)
+ * (a label outside that range reads nothing and gives a NaN row loss);
+ * row_loss: device f32 [B] (required: it is also the scratch of the mean);
+ * loss_mean: device f32 [1]; dlogits: device [B x C] (d_type, ld_d) or NULL;
+ * argmax: device int32 [B] or NULL.  C <= 4096.
+ * ---------------------------------------------------------------------- */
+int softmax_xent_fwd_bwd(const float *logits, int64_t B, int64_t C, int64_t ld,
+                         const int32_t *labels, float grad_scale, float *loss_mean,
+                         float *row_loss, void *dlogits, int64_t ld_d, int32_t d_type,
+                         int32_t *argmax, ge_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * rmsnorm_fwd_bwd -- RMSNorm over rows of width D, FP32 statistics
+ * [CAT] "The Debugging Lesson Was Numerical": normalisation statistics stay
+ * FP32; [MK] "What Worked": RMSNorm opens the MLP block.
+ *   GE_FWD: r[i] = 1/sqrt(mean_j x[i,j]^2 + eps);  y = x * r (* gamma[j])
+ *   GE_BWD: xh = x * r;  g = dy (* gamma);  c = mean_j g xh;
+ *           dx = r * (g - xh * c) (+ dres);  dgamma[j] = sum_i dy xh (optional)
+ * x: device [rows x D] (x_type, ld_x); y: (y_type, ld_y); r: device f32 [rows];
+ * dy: (dy_type, ld_dy); dres: (dres_type, ld_dres) or NULL; dx: (dx_type,
+ * ld_dx); gamma: device f32 [D] or NULL; dgamma: device f32 [D] or NULL (needs
+ * workspace of rmsnorm_workspace_bytes(rows, D) bytes).  1 <= D <= 4096.
+ * ---------------------------------------------------------------------- */
+#define GE_FWD 0
+#define GE_BWD 1
+typedef struct ge_rmsnorm_args {
+  int32_t pass; /* GE_FWD or GE_BWD */
+  int64_t rows, D;
+  float eps;
+  const void *x;
+  int64_t ld_x;
+  int32_t x_type;
+  const float *gamma; /* or NULL */
+  void *y;            /* FWD output */
+  int64_t ld_y;
+  int32_t y_type;
+  float *r;       /* FWD output / BWD input, f32 [rows] */
+  const void *dy; /* BWD input */
+  int64_t ld_dy;
+  int32_t dy_type;
+  const void *dres; /* BWD optional residual gradient added to dx */
+  int64_t ld_dres;
+  int32_t dres_type;
+  void *dx; /* BWD output */
+  int64_t ld_dx;
+  int32_t dx_type;
+  float *dgamma; /* BWD optional */
+  void *workspace;
+  int64_t workspace_bytes;
+} ge_rmsnorm_args;
+
+int rmsnorm_fwd_bwd(const ge_rmsnorm_args *args, ge_stream_t stream);
+int64_t rmsnorm_workspace_bytes(int64_t rows, int64_t D);
+
+/* ------------------------------------------------------------------------
+ * sgd_momentum -- one update over a flat parameter buffer
+ * [CAP] "Read the worked reference": all parameter tensors live in one flat
+ * buffer; vel = momentum * v - lr * g; v = vel; w += vel, for every element.
+ * w, g, v: device f32 [n] (w, v updated in place); w_lowp: device [n] of
+ * lowp_type (F16 or BF16) receiving convert(w_new), or NULL.
+ * ---------------------------------------------------------------------- */
+int sgd_momentum(float *w, const float *g, float *v, float lr, float momentum, int64_t n,
+                 void *w_lowp, int32_t lowp_type, ge_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mlp_train_step -- one SGD-momentum step of a dense ReLU MLP
+ * [CAP] "The minimum model", "Work through the backward pass", "Read the
+ * worked reference":  H_l = ReLU(H_{l-1} W_l + b_l), Z = H_{L-1} W_L + b_L,
+ * stable softmax CE (mean over the batch), dW_l = H_{l-1}^T G_l,
+ * db_l = colsum(G_l), G_{l-1} = (G_l W_l^T) * (H_{l-1} > 0), then one
+ * momentum update over the flat buffer.
+ *
+ * Flat parameter layout: [W1, b1, W2, b2, ...], W_l row-major
+ * [dims[l-1] x dims[l]], biases f32; params / grads / velocity are device f32
+ * [mlp_param_count].  storage = GE_F32: X f32, everything stored in FP32,
+ * G = (p - onehot)/B.  storage = GE_F16: X f16, GEMMs read the FP16 working
+ * copy `params_lowp` (device f16 [mlp_param_count], kept in step by the
+ * update), hidden activations, G = p - onehot (unscaled) and dH are FP16,
+ * logits FP32, and 1/B is applied in the weight/bias gradient epilogues.
+ * labels: device int32 [B]; loss_out: device f32 [1] (mean loss).
+ * Workspace: mlp_workspace_bytes(desc, B) bytes; its layout is reported by
+ * mlp_workspace_offsets (byte offsets of H_1..H_{L-1}, Z, G, row_loss).
+ * ---------------------------------------------------------------------- */
+typedef struct ge_mlp_desc {
+  int32_t n_layers;     /* number of weight layers L >= 1 */
+  const int64_t *dims;  /* host [L + 1] widths, dims[0] = input, dims[L] = classes */
+  int32_t storage;      /* GE_F32 or GE_F16 */
+} ge_mlp_desc;
+
+typedef struct ge_mlp_buffers {
+  float *params;      /* device f32 [P] */
+  float *grads;       /* device f32 [P] (written) */
+  float *velocity;    /* device f32 [P] */
+  void *params_lowp;  /* device f16 [P] (GE_F16 storage) or NULL */
+  void *workspace;    /* device */
+  int64_t workspace_bytes;
+} ge_mlp_buffers;
+
+int64_t mlp_param_count(int32_t n_layers, const int64_t *dims);
+int64_t mlp_workspace_bytes(const ge_mlp_desc *desc, int64_t B);
+/* writes n_layers + 2 byte offsets: H_1 .. H_{L-1}, Z (f32), G, row_loss (f32) */
+int mlp_workspace_offsets(const ge_mlp_desc *desc, int64_t B, int64_t *offsets, int32_t n);
+int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const void *X,
+                   const int32_t *labels, int64_t B, float lr, float momentum,
+                   float *loss_out, ge_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GEMM_EPILOGUE_H */
