@@ -56,6 +56,7 @@ __device__ __forceinline__ void load4_any(const void *p, int64_t i, int t, bool 
       v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
     }
   } else {
+#pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = load_any(p, i + j, t);
   }
 }
@@ -72,6 +73,7 @@ __device__ __forceinline__ void store4_any(void *p, int64_t i, int t, bool vec, 
       *(bf16x4 *)((bf16_t *)p + i) = x;
     }
   } else {
+#pragma unroll
     for (int j = 0; j < 4; ++j) store_any(p, i + j, t, v[j]);
   }
 }

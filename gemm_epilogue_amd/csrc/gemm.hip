@@ -10,13 +10,18 @@
 // epilogues.
 //
 // Design (ours, not the pages'): a block of 4 wavefronts computes a BM x BN
-// tile; A and B tiles of BK along k are staged through LDS, double-buffered,
-// always stored k-contiguous ([row][k], rows padded by 16 bytes) so each MFMA
-// fragment is one 16-byte LDS read per lane.  Operands that are contiguous
-// along m/n in memory (B of NN, both of TN) are transposed in registers on
-// their way into LDS.  MFMA 16x16 tiles are issued with the B tile in the
-// instruction's first operand slot, so each lane ends up owning four
-// consecutive columns of one output row (16-byte FP32 / 8-byte 16-bit stores).
+// tile (256x256, 128x128 or 64x64 by problem size); A and B tiles of BK along
+// k are staged through LDS, double-buffered, always stored k-contiguous
+// ([row][k], rows padded by 16 bytes) so each MFMA fragment is one 16-byte
+// LDS read per lane and the 16 lanes that read one fragment hit 16 different
+// bank groups.  Operands contiguous along m/n in memory (B of NN, both of TN)
+// are transposed in registers on their way into LDS; the thread mapping of
+// that transpose puts consecutive lanes on consecutive 16-byte k-chunks so the
+// transposed writes are conflict-free too.  Tiles entirely inside the matrix
+// use unconditional 16-byte loads and stores (a block-uniform branch); tiles on
+// the M/N edge and the partial last k-tile use checked element loads.  MFMA
+// 16x16 tiles are issued with the B tile in the instruction's first operand
+// slot, so each lane owns four consecutive columns of one output row.
 // FP16/BF16 use v_mfma_f32_16x16x32_{f16,bf16}; FP32 uses v_mfma_f32_16x16x4_f32.
 // Split-K writes FP32 partials to a workspace and a finishing kernel sums
 // them in split order, then applies the same epilogue.
@@ -61,25 +66,31 @@ struct GemmParams {
 };
 
 // Epilogue for four consecutive columns n..n+3 of row m (FP32 values v).
-__device__ __forceinline__ void epilogue4(const EpiParams &e, int m, int n, float v[4]) {
-  if (m >= e.M || n >= e.N) return;
-  const bool full = (n + 3) < e.N;
+// `fast`: the four columns are inside the matrix and every access is aligned.
+__device__ __forceinline__ void epilogue4(const EpiParams &e, int m, int n, f32x4 acc, bool fast) {
+  if (!fast && (m >= e.M || n >= e.N)) return;
+  const bool full = fast || (n + 3) < e.N;
+  float v[4] = {acc[0], acc[1], acc[2], acc[3]};
   float b[4] = {0.f, 0.f, 0.f, 0.f};
   if (e.bias) {
     if (full && e.bias_vec) {
       f32x4 x = *(const f32x4 *)(e.bias + n);
       b[0] = x[0]; b[1] = x[1]; b[2] = x[2]; b[3] = x[3];
     } else {
+#pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = (n + j < e.N) ? e.bias[n + j] : 0.f;
     }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) v[j] = e.alpha * v[j] + b[j];
   if (e.pre) {
-    if (full) store4_any(e.pre, (int64_t)m * e.ld_pre + n, e.pre_type, e.pre_vec, v);
-    else
+    if (full) {
+      store4_any(e.pre, (int64_t)m * e.ld_pre + n, e.pre_type, e.pre_vec, v);
+    } else {
+#pragma unroll
       for (int j = 0; j < 4; ++j)
         if (n + j < e.N) store_any(e.pre, (int64_t)m * e.ld_pre + n + j, e.pre_type, v[j]);
+    }
   }
   if (e.act == GE_ACT_RELU) {
 #pragma unroll
@@ -87,15 +98,18 @@ __device__ __forceinline__ void epilogue4(const EpiParams &e, int m, int n, floa
   } else if (e.act == GE_ACT_LRELU_SQ) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float t = v[j] > 0.f ? v[j] : e.slope * v[j];
+      const float t = v[j] > 0.f ? v[j] : e.slope * v[j];
       v[j] = t * t;
     }
   } else if (e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD) {
     float a[4];
-    if (full) load4_any(e.aux, (int64_t)m * e.ld_aux + n, e.aux_type, e.aux_vec, a);
-    else
+    if (full) {
+      load4_any(e.aux, (int64_t)m * e.ld_aux + n, e.aux_type, e.aux_vec, a);
+    } else {
+#pragma unroll
       for (int j = 0; j < 4; ++j)
         a[j] = (n + j < e.N) ? load_any(e.aux, (int64_t)m * e.ld_aux + n + j, e.aux_type) : 0.f;
+    }
     if (e.act == GE_ACT_RELU_MASK_BWD) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = a[j] > 0.f ? v[j] : 0.f;
@@ -107,17 +121,23 @@ __device__ __forceinline__ void epilogue4(const EpiParams &e, int m, int n, floa
   }
   if (e.res) {
     float r[4];
-    if (full) load4_any(e.res, (int64_t)m * e.ld_res + n, e.res_type, e.res_vec, r);
-    else
+    if (full) {
+      load4_any(e.res, (int64_t)m * e.ld_res + n, e.res_type, e.res_vec, r);
+    } else {
+#pragma unroll
       for (int j = 0; j < 4; ++j)
         r[j] = (n + j < e.N) ? load_any(e.res, (int64_t)m * e.ld_res + n + j, e.res_type) : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] += r[j];
   }
-  if (full) store4_any(e.C, (int64_t)m * e.ldc + n, e.c_type, e.c_vec, v);
-  else
+  if (full) {
+    store4_any(e.C, (int64_t)m * e.ldc + n, e.c_type, e.c_vec, v);
+  } else {
+#pragma unroll
     for (int j = 0; j < 4; ++j)
       if (n + j < e.N) store_any(e.C, (int64_t)m * e.ldc + n + j, e.c_type, v[j]);
+  }
 }
 
 // ---- MFMA wrappers: acc += hwA * hwB over one 16-byte-per-lane k chunk -----
@@ -147,37 +167,53 @@ template <> struct Frag<float> {
   }
 };
 
-// raw 16-byte vector of T elements
-struct alignas(16) Raw16 {
-  uint32_t w[4];
-};
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <typename T> __device__ __forceinline__ T zero_of() { return (T)0.f; }
+// element e of a 16-byte vector holding T values, as raw bits
+template <typename T> __device__ __forceinline__ uint32_t elem_bits(const u32x4 &v, int e) {
+  if constexpr (sizeof(T) == 4) return v[e];
+  else return (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
+}
+template <typename T> __device__ __forceinline__ uint32_t bits_of(T x) {
+  if constexpr (sizeof(T) == 4) return __builtin_bit_cast(uint32_t, x);
+  else return (uint32_t)__builtin_bit_cast(uint16_t, x);
+}
 
 // ---- tile loaders ------------------------------------------------------------
 // k-contiguous source: R rows (m or n) x BK, each row contiguous along k.
+// Thread t moves vectors v = t + i*NT: row v / VPR, 16-byte chunk v % VPR.
 template <typename T, int R, int BK, int NT> struct LoaderKC {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int VPR = BK / VEC;  // vectors per row
   static constexpr int NV = R * VPR / NT;
   static_assert(NV >= 1 && (R * VPR) % NT == 0, "tile / thread mismatch");
-  Raw16 r[NV];
+  u32x4 r[NV];
 
-  __device__ __forceinline__ void load(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
-                                       int kmax, bool vec, int tid) {
+  __device__ __forceinline__ void load_fast(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = tid + i * NT;
-      const int row = v / VPR, kv = v % VPR;
-      const int gr = r0 + row, gk = k0 + kv * VEC;
-      if (vec && gr < rmax && gk + VEC <= kmax) {
-        r[i] = *(const Raw16 *)(p + (int64_t)gr * ld + gk);
-      } else {
-        T tmp[VEC];
+      r[i] = *(const u32x4 *)(p + (int64_t)(r0 + v / VPR) * ld + k0 + (v % VPR) * VEC);
+    }
+  }
+  __device__ __forceinline__ void load_checked(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
+                                               int kmax, bool vec, int tid) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          tmp[e] = (gr < rmax && gk + e < kmax) ? p[(int64_t)gr * ld + gk + e] : zero_of<T>();
-        r[i] = *(Raw16 *)tmp;
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + i * NT;
+      const int gr = r0 + v / VPR, gk = k0 + (v % VPR) * VEC;
+      if (vec && gr < rmax && gk + VEC <= kmax) {
+        r[i] = *(const u32x4 *)(p + (int64_t)gr * ld + gk);
+      } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t b = (gr < rmax && gk + e < kmax) ? bits_of<T>(p[(int64_t)gr * ld + gk + e]) : 0u;
+          if constexpr (sizeof(T) == 4) w[e] = b;
+          else w[e >> 1] |= b << (16 * (e & 1));
+        }
+        r[i] = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
   }
@@ -185,56 +221,72 @@ template <typename T, int R, int BK, int NT> struct LoaderKC {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = tid + i * NT;
-      const int row = v / VPR, kv = v % VPR;
-      *(Raw16 *)(s + row * stride + kv * VEC) = r[i];
+      *(u32x4 *)(s + (v / VPR) * stride + (v % VPR) * VEC) = r[i];
     }
   }
 };
 
 // m/n-contiguous source: BK k-rows, each contiguous along the R dimension.
-// Each thread reads KB consecutive k-rows of one 16-byte vector and writes
-// them transposed: VEC LDS rows of KB k-values.
+// Thread t owns k-group kg = t % NKG (KB consecutive k-rows) and vector
+// rv = t / NKG (VEC consecutive rows of the tile); it writes VEC LDS rows of
+// KB k-values.  Consecutive lanes take consecutive k-groups, so one LDS write
+// instruction spreads over distinct 16-byte bank groups.
 template <typename T, int R, int BK, int NT> struct LoaderMC {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int RV = R / VEC;  // vectors per k-row
   static constexpr int KB = BK * RV / NT;
-  static_assert(KB >= 1 && (BK * RV) % NT == 0 && BK % KB == 0, "tile / thread mismatch");
-  T x[KB][VEC];
+  static constexpr int NKG = BK / KB;
+  static constexpr int W = KB * sizeof(T) / 4;  // dwords per transposed row piece
+  static_assert(KB >= 2 && (BK * RV) % NT == 0 && BK % KB == 0, "tile / thread mismatch");
+  static_assert(W == 1 || W == 2 || W % 4 == 0, "transposed piece must be 4, 8 or 16n bytes");
+  u32x4 x[KB];
 
-  __device__ __forceinline__ void load(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
-                                       int kmax, bool vec, int tid) {
-    const int rv = tid % RV, kg = tid / RV;
+  __device__ __forceinline__ void load_fast(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid) {
+    const int kg = tid % NKG, rv = tid / NKG;
+    const T *base = p + (int64_t)(k0 + kg * KB) * ld + r0 + rv * VEC;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) x[j] = *(const u32x4 *)(base + (int64_t)j * ld);
+  }
+  __device__ __forceinline__ void load_checked(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
+                                               int kmax, bool vec, int tid) {
+    const int kg = tid % NKG, rv = tid / NKG;
     const int gr = r0 + rv * VEC;
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int gk = k0 + kg * KB + j;
       if (vec && gk < kmax && gr + VEC <= rmax) {
-        Raw16 t = *(const Raw16 *)(p + (int64_t)gk * ld + gr);
-        const T *tt = (const T *)&t;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[j][e] = tt[e];
+        x[j] = *(const u32x4 *)(p + (int64_t)gk * ld + gr);
       } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          x[j][e] = (gk < kmax && gr + e < rmax) ? p[(int64_t)gk * ld + gr + e] : zero_of<T>();
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t b = (gk < kmax && gr + e < rmax) ? bits_of<T>(p[(int64_t)gk * ld + gr + e]) : 0u;
+          if constexpr (sizeof(T) == 4) w[e] = b;
+          else w[e >> 1] |= b << (16 * (e & 1));
+        }
+        x[j] = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
   }
   __device__ __forceinline__ void store(T *s, int stride, int tid) const {
-    const int rv = tid % RV, kg = tid / RV;
+    const int kg = tid % NKG, rv = tid / NKG;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      T col[KB];
+      // column e of the KB x VEC block: KB k-values of tile row rv*VEC + e
+      uint32_t w[W];
 #pragma unroll
-      for (int j = 0; j < KB; ++j) col[j] = x[j][e];
-      T *dst = s + (rv * VEC + e) * stride + kg * KB;
-      if constexpr (KB * sizeof(T) == 16) {
-        *(Raw16 *)dst = *(Raw16 *)col;
-      } else if constexpr (KB * sizeof(T) == 8) {
-        *(uint2 *)dst = *(uint2 *)col;
+      for (int q = 0; q < W; ++q) {
+        if constexpr (sizeof(T) == 4) w[q] = elem_bits<T>(x[q], e);
+        else w[q] = elem_bits<T>(x[2 * q], e) | (elem_bits<T>(x[2 * q + 1], e) << 16);
+      }
+      uint32_t *dst = (uint32_t *)(s + (rv * VEC + e) * stride + kg * KB);
+      if constexpr (W == 1) {
+        dst[0] = w[0];
+      } else if constexpr (W == 2) {
+        *(u32x2 *)dst = u32x2{w[0], w[1]};
       } else {
 #pragma unroll
-        for (int j = 0; j < KB; ++j) dst[j] = col[j];
+        for (int q = 0; q < W; q += 4) *(u32x4 *)(dst + q) = u32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
       }
     }
   }
@@ -245,25 +297,34 @@ template <typename T, int R, int BK, int NT> struct Loader<T, true, R, BK, NT> :
 template <typename T, int R, int BK, int NT> struct Loader<T, false, R, BK, NT> : LoaderMC<T, R, BK, NT> {};
 
 // ---- the kernel ---------------------------------------------------------------
-template <typename T, int LAYOUT, int BM, int BN, int BK>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
-  constexpr int NT = 256;
+template <typename T, int LAYOUT, int BM, int BN, int BK, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm_kernel(GemmParams p) {
+  constexpr int NT = 64 * WGM * WGN;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KCH = 4 * VEC;  // k covered by one 16-byte-per-lane fragment
   constexpr int STRIDE = BK + VEC;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr bool A_KC = (LAYOUT != GE_TN);
   constexpr bool B_KC = (LAYOUT == GE_NT);
   static_assert(BK % KCH == 0, "BK must hold whole fragments");
   typedef typename Frag<T>::V V;
 
-  __shared__ __attribute__((aligned(16))) T sA[2][BM * STRIDE];
-  __shared__ __attribute__((aligned(16))) T sB[2][BN * STRIDE];
+  // operand tiles (double-buffered); after the k loop the same memory stages
+  // the FP32 accumulator tile for the epilogue
+  constexpr int OPER_BYTES = 2 * (BM + BN) * STRIDE * (int)sizeof(T);
+  constexpr int NPASS = BM >= 256 ? 2 : 1;  // row passes of the staged epilogue
+  constexpr int RP = BM / NPASS;
+  constexpr int CSTRIDE = BN + 4;  // floats per staged row (16-byte pad)
+  static_assert(RP * CSTRIDE * 4 <= OPER_BYTES, "staged tile must fit in the operand buffers");
+  static_assert(BM / WGM <= RP && RP % (BM / WGM) == 0, "a wave's rows must fall in one pass");
+  __shared__ __attribute__((aligned(16))) char smem[OPER_BYTES];
+  T(*sA)[BM * STRIDE] = (T(*)[BM * STRIDE])smem;
+  T(*sB)[BN * STRIDE] = (T(*)[BN * STRIDE])(smem + 2 * BM * STRIDE * sizeof(T));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave >> 1) * WTM, wn0 = (wave & 1) * WTN;
+  const int wm0 = (wave / WGN) * WTM, wn0 = (wave % WGN) * WTN;
 
   // block -> tile: spread consecutive tiles over one XCD, then group along M
   int bid = blockIdx.x;
@@ -278,14 +339,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   const int bm0 = tm * BM, bn0 = tn * BN;
 
   const int nk_total = (p.K + BK - 1) / BK;
+  const int nk_full = p.K / BK;
   const int kt0 = blockIdx.z * p.ktiles_per_split;
   const int kt1 = min(nk_total, kt0 + p.ktiles_per_split);
+  const bool interior = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && p.a_vec && p.b_vec;
 
   const T *__restrict__ Ap = (const T *)p.A;
   const T *__restrict__ Bp = (const T *)p.B;
 
   Loader<T, A_KC, BM, BK, NT> la;
   Loader<T, B_KC, BN, BK, NT> lb;
+
+  auto load_tile = [&](int kt) {
+    if (interior && kt < nk_full) {
+      la.load_fast(Ap, p.lda, bm0, kt * BK, tid);
+      lb.load_fast(Bp, p.ldb, bn0, kt * BK, tid);
+    } else {
+      la.load_checked(Ap, p.lda, bm0, p.M, kt * BK, p.K, p.a_vec, tid);
+      lb.load_checked(Bp, p.ldb, bn0, p.N, kt * BK, p.K, p.b_vec, tid);
+    }
+  };
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -294,29 +367,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (kt0 < kt1) {
-    la.load(Ap, p.lda, bm0, p.M, kt0 * BK, p.K, p.a_vec, tid);
-    lb.load(Bp, p.ldb, bn0, p.N, kt0 * BK, p.K, p.b_vec, tid);
+    load_tile(kt0);
     la.store(sA[0], STRIDE, tid);
     lb.store(sB[0], STRIDE, tid);
     __syncthreads();
   }
+  const int arow = (wm0 + (lane & 15)) * STRIDE + (lane >> 4) * VEC;
+  const int brow = (wn0 + (lane & 15)) * STRIDE + (lane >> 4) * VEC;
   for (int kt = kt0; kt < kt1; ++kt) {
     const int cur = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
-    if (more) {
-      la.load(Ap, p.lda, bm0, p.M, (kt + 1) * BK, p.K, p.a_vec, tid);
-      lb.load(Bp, p.ldb, bn0, p.N, (kt + 1) * BK, p.K, p.b_vec, tid);
-    }
-    const T *a_s = sA[cur];
-    const T *b_s = sB[cur];
+    if (more) load_tile(kt + 1);
+    const T *a_s = sA[cur] + arow;
+    const T *b_s = sB[cur] + brow;
 #pragma unroll
     for (int c = 0; c < BK / KCH; ++c) {
-      const int koff = c * KCH + (lane >> 4) * VEC;
       V af[FM], bf[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *(const V *)(a_s + (wm0 + i * 16 + (lane & 15)) * STRIDE + koff);
+      for (int i = 0; i < FM; ++i) af[i] = *(const V *)(a_s + i * 16 * STRIDE + c * KCH);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = *(const V *)(b_s + (wn0 + j * 16 + (lane & 15)) * STRIDE + koff);
+      for (int j = 0; j < FN; ++j) bf[j] = *(const V *)(b_s + j * 16 * STRIDE + c * KCH);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -329,26 +399,45 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  // lane owns C[m][n..n+3] of each 16x16 fragment
+  // Epilogue: the lane owning C[m][n..n+3] of each 16x16 fragment writes it
+  // to the staged tile in LDS; then all threads walk the staged rows, four
+  // consecutive columns per thread, so global stores are whole-row coalesced.
+  const EpiParams &e = p.ep;
+  const bool fast = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && e.c_vec && (!e.aux || e.aux_vec) &&
+                    (!e.res || e.res_vec) && (!e.pre || e.pre_vec) && (!e.bias || e.bias_vec);
+  float *cs = (float *)smem;
+  float *part = p.splits > 1 ? p.partial + (int64_t)blockIdx.z * p.M * p.N : nullptr;
+  const bool pvec = (p.N & 3) == 0;
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if (wm0 / RP == pass) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = bm0 + wm0 + i * 16 + (lane & 15);
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = bn0 + wn0 + j * 16 + (lane >> 4) * 4;
-      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      if (p.splits == 1) {
-        epilogue4(p.ep, m, n, v);
+        for (int j = 0; j < FN; ++j) {
+          const int row = wm0 - pass * RP + i * 16 + (lane & 15);
+          const int col = wn0 + j * 16 + (lane >> 4) * 4;
+          *(f32x4 *)(cs + row * CSTRIDE + col) = acc[i][j];
+        }
+    }
+    __syncthreads();
+    for (int g = tid; g < RP * (BN / 4); g += NT) {
+      const int r = g / (BN / 4), c = (g % (BN / 4)) * 4;
+      const f32x4 v = *(const f32x4 *)(cs + r * CSTRIDE + c);
+      const int m = bm0 + pass * RP + r, n = bn0 + c;
+      if (part == nullptr) {
+        epilogue4(e, m, n, v, fast);
       } else if (m < p.M && n < p.N) {
-        float *dst = p.partial + ((int64_t)blockIdx.z * p.M + m) * p.N + n;
-        if (n + 3 < p.N && (p.N & 3) == 0) {
-          *(f32x4 *)dst = acc[i][j];
+        float *dst = part + (int64_t)m * p.N + n;
+        if (pvec && n + 3 < p.N) {
+          *(f32x4 *)dst = v;
         } else {
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) dst[e] = v[e];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < p.N) dst[q] = v[q];
         }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -361,38 +450,41 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p) {
   const int n = (int)(idx % groups) * 4;
   const int64_t mn = (int64_t)p.M * p.N;
   const float *src = p.partial + (int64_t)m * p.N + n;
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
   const bool vec = (n + 3 < p.N) && (p.N & 3) == 0;
   for (int s = 0; s < p.splits; ++s) {
     if (vec) {
-      f32x4 x = *(const f32x4 *)(src + s * mn);
-      v[0] += x[0]; v[1] += x[1]; v[2] += x[2]; v[3] += x[3];
+      v += *(const f32x4 *)(src + s * mn);
     } else {
-      for (int e = 0; e < 4; ++e)
-        if (n + e < p.N) v[e] += src[s * mn + e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (n + q < p.N) v[q] += src[s * mn + q];
     }
   }
-  epilogue4(p.ep, m, n, v);
+  epilogue4(p.ep, m, n, v, false);
 }
 
 // ---- host launcher --------------------------------------------------------------
 namespace {
 
 struct Plan {
-  int big;  // 1: 128x128 tiles, 0: 64x64 tiles
-  int BM, BN, BK;
+  int tile;  // 256, 128 or 64 (square tiles)
+  int BK;
   int tiles_m, tiles_n, nk, splits, kps;
 };
+
+int64_t ntiles(int64_t M, int64_t N, int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); }
 
 Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   Plan pl;
   const int bk = ab_type == GE_F32 ? 32 : 64;
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-  pl.big = (t128 >= 192) ? 1 : 0;
-  pl.BM = pl.BN = pl.big ? 128 : 64;
+  // the largest square tile that still gives most of the 256 CUs a tile
+  if (ntiles(M, N, 256) >= 192) pl.tile = 256;
+  else if (ntiles(M, N, 128) >= 160) pl.tile = 128;
+  else pl.tile = 64;
   pl.BK = bk;
-  pl.tiles_m = (int)((M + pl.BM - 1) / pl.BM);
-  pl.tiles_n = (int)((N + pl.BN - 1) / pl.BN);
+  pl.tiles_m = (int)((M + pl.tile - 1) / pl.tile);
+  pl.tiles_n = (int)((N + pl.tile - 1) / pl.tile);
   pl.nk = (int)((K + bk - 1) / bk);
   int s = 1;
   if (split_k >= 1) {
@@ -407,9 +499,8 @@ Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
     }
   }
   s = std::max(1, std::min(s, std::max(1, pl.nk)));
-  pl.kps = (pl.nk + s - 1) / std::max(1, s);
+  pl.kps = (pl.nk + s - 1) / s;
   pl.splits = pl.kps > 0 ? (pl.nk + pl.kps - 1) / pl.kps : 1;
-  if (pl.splits < 1) pl.splits = 1;
   return pl;
 }
 
@@ -417,10 +508,12 @@ template <typename T, int LAYOUT>
 void launch_t(const Plan &pl, const GemmParams &gp, hipStream_t s) {
   dim3 grid(pl.tiles_m * pl.tiles_n, 1, pl.splits);
   constexpr int BK = sizeof(T) == 4 ? 32 : 64;
-  if (pl.big)
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 128, 128, BK>), grid, dim3(256), 0, s, gp);
+  if (pl.tile == 256)
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 256, 256, BK, 2, 4>), grid, dim3(512), 0, s, gp);
+  else if (pl.tile == 128)
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 128, 128, BK, 2, 2>), grid, dim3(256), 0, s, gp);
   else
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 64, 64, BK>), grid, dim3(256), 0, s, gp);
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 64, 64, BK, 2, 2>), grid, dim3(256), 0, s, gp);
 }
 
 template <typename T>
@@ -462,8 +555,8 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
   if (pl.splits > 1) {
     const int64_t need = (int64_t)pl.splits * a.M * a.N * 4;
     if (a.workspace == nullptr || a.workspace_bytes < need || ((uintptr_t)a.workspace % 16) != 0) {
-      set_error("gemm_bias_act: split-K over %d splits needs %lld workspace bytes (16-byte aligned)", pl.splits,
-                (long long)need);
+      set_error("gemm_bias_act: split-K over %d splits needs %lld workspace bytes (16-byte aligned)",
+                pl.splits, (long long)need);
       return GE_E_WORKSPACE;
     }
     gp.partial = (float *)a.workspace;
@@ -487,10 +580,13 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
   e.pre_type = a.pre_type;
   e.M = (int)a.M;
   e.N = (int)a.N;
-  e.aux_vec = a.aux ? vec_aligned(a.aux, a.ld_aux, dtype_size(a.aux_type), 4 * dtype_size(a.aux_type)) : 0;
-  e.res_vec = a.residual ? vec_aligned(a.residual, a.ld_res, dtype_size(a.res_type), 4 * dtype_size(a.res_type)) : 0;
-  e.c_vec = vec_aligned(a.C, a.ldc, dtype_size(a.c_type), 4 * dtype_size(a.c_type));
-  e.pre_vec = a.pre ? vec_aligned(a.pre, a.ld_pre, dtype_size(a.pre_type), 4 * dtype_size(a.pre_type)) : 0;
+  auto al4 = [](const void *ptr, int64_t ld, int t) {
+    return ptr ? (int)vec_aligned(ptr, ld, dtype_size(t), 4 * dtype_size(t)) : 0;
+  };
+  e.aux_vec = al4(a.aux, a.ld_aux, a.aux_type);
+  e.res_vec = al4(a.residual, a.ld_res, a.res_type);
+  e.c_vec = al4(a.C, a.ldc, a.c_type);
+  e.pre_vec = al4(a.pre, a.ld_pre, a.pre_type);
   e.bias_vec = a.bias ? (((uintptr_t)a.bias % 16) == 0) : 0;
 
   if (a.ab_type == GE_F16) launch_layout<half_t>(a.layout, pl, gp, s);

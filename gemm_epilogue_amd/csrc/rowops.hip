@@ -137,20 +137,35 @@ __global__ __launch_bounds__(256) void xent_rows_kernel(const float *__restrict_
     const int oi = __shfl_xor(mi, o, 64);
     if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
   }
-  float s = 0.f;
-  for (int c = lane; c < C; c += 64) s += expf(z[c] - m);
-  s = wave_sum(s);
-  const float lse = m + logf(s);
+  // The sum of exp(z - m) is 1 (the maximum's own term) plus the sum of the
+  // other terms, s_rest.  Keeping s_rest apart avoids two cancellations in
+  // FP32 when one class dominates: lse - m = log1p(s_rest) instead of
+  // log(1 + s_rest), and for the label class p - 1 = -(sum of the other
+  // classes' terms) / s instead of a subtraction from 1.
   const int y = labels[row];
+  const bool yok = (unsigned)y < (unsigned)C;
+  float s_rest = 0.f, e_y = 0.f;
+  for (int c = lane; c < C; c += 64) {
+    const float e = expf(z[c] - m);
+    if (c != mi) s_rest += e;
+    if (c == y) e_y = e;
+  }
+  s_rest = wave_sum(s_rest);
+  e_y = wave_sum(e_y);  // exactly one lane holds it
+  const float l1p = log1pf(s_rest);
+  const float lse = m + l1p;
+  const float s = 1.f + s_rest;
   if (lane == 0) {
     // a label outside [0, C) reads nothing and yields a NaN row loss
-    row_loss[row] = ((unsigned)y < (unsigned)C) ? lse - z[y] : NAN;
+    row_loss[row] = yok ? (m - z[y]) + l1p : NAN;
     if (amax) amax[row] = mi;
   }
   if (dZ) {
+    // sum of the terms of every class but the label's
+    const float s_noty = (y == mi) ? s_rest : s - e_y;
     for (int c = lane; c < C; c += 64) {
-      const float p = expf(z[c] - lse);
-      store_any(dZ, (int64_t)row * ldd + c, dt, gscale * (p - (c == y ? 1.f : 0.f)));
+      const float g = (c == y) ? -(s_noty / s) : expf(z[c] - lse);
+      store_any(dZ, (int64_t)row * ldd + c, dt, gscale * g);
     }
   }
 }

@@ -133,13 +133,15 @@ int64_t mlp_workspace_bytes(const ge_mlp_desc *desc, int64_t B) {
 
 int mlp_workspace_offsets(const ge_mlp_desc *desc, int64_t B, int64_t *offsets, int32_t n) {
   CHECK(desc_ok(desc) && B >= 0, "mlp_workspace_offsets: bad descriptor or batch");
-  CHECK(offsets != nullptr && n >= desc->n_layers + 2, "mlp_workspace_offsets: need n_layers + 2 slots");
+  CHECK(offsets != nullptr && n >= desc->n_layers + 4, "mlp_workspace_offsets: need n_layers + 4 slots");
   MlpLayout L = layout_of(desc, B);
   int i = 0;
   for (int64_t o : L.h_off) offsets[i++] = o;
   offsets[i++] = L.z_off;
   offsets[i++] = L.g_off;
   offsets[i++] = L.loss_off;
+  offsets[i++] = L.dh_off[0];
+  offsets[i++] = L.dh_off[1];
   return GE_OK;
 }
 

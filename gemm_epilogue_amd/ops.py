@@ -218,20 +218,30 @@ class MLPTrainer:
         return self.loss
 
     def workspace_views(self, B=None):
-        """Views of the stored activations H_1..H_{L-1}, logits Z, dZ and row losses."""
+        """Views of the stored activations H_1..H_{L-1}, logits Z, dZ, row losses
+        and the masked hidden gradients dH_l still held after the step (the
+        two gradient buffers alternate, so with more than three layers only
+        the last two written survive; the others are None)."""
         B = self.batch if B is None else B
         L = len(self.dims) - 1
-        offs = (C.c_int64 * (L + 2))()
-        check(lib.mlp_workspace_offsets(C.byref(self.desc), B, offs, L + 2), "mlp_workspace_offsets")
+        offs = (C.c_int64 * (L + 4))()
+        check(lib.mlp_workspace_offsets(C.byref(self.desc), B, offs, L + 4), "mlp_workspace_offsets")
         ws = self.workspace
-        out = {"H": []}
-        for l in range(1, L):
-            n = B * self.dims[l]
-            es = 2 if self.storage == torch.float16 else 4
-            out["H"].append(ws[offs[l - 1]:offs[l - 1] + n * es].view(self.storage).view(B, self.dims[l]))
-        Cn = self.dims[-1]
-        out["Z"] = ws[offs[L - 1]:offs[L - 1] + B * Cn * 4].view(torch.float32).view(B, Cn)
         es = 2 if self.storage == torch.float16 else 4
-        out["G"] = ws[offs[L]:offs[L] + B * Cn * es].view(self.storage).view(B, Cn)
+
+        def view(off, rows, cols, dt, size):
+            return ws[off:off + rows * cols * size].view(dt).view(rows, cols)
+
+        out = {"H": [view(offs[l - 1], B, self.dims[l], self.storage, es) for l in range(1, L)]}
+        Cn = self.dims[-1]
+        out["Z"] = view(offs[L - 1], B, Cn, torch.float32, 4)
+        out["G"] = view(offs[L], B, Cn, self.storage, es)
         out["row_loss"] = ws[offs[L + 1]:offs[L + 1] + B * 4].view(torch.float32)
+        # dH_{L-1} went to buffer 0, dH_{L-2} to buffer 1, dH_{L-3} to buffer 0, ...
+        dH = [None] * (L - 1)
+        for l in range(L - 1, 0, -1):
+            k = (L - 1 - l) % 2
+            if L - 1 - l >= (L - 1) - 2:       # among the last two written
+                dH[l - 1] = view(offs[L + 2 + k], B, self.dims[l], self.storage, es)
+        out["dH"] = dH
         return out

@@ -238,7 +238,9 @@ int sgd_momentum(float *w, const float *g, float *v, float lr, float momentum, i
  * logits FP32, and 1/B is applied in the weight/bias gradient epilogues.
  * labels: device int32 [B]; loss_out: device f32 [1] (mean loss).
  * Workspace: mlp_workspace_bytes(desc, B) bytes; its layout is reported by
- * mlp_workspace_offsets (byte offsets of H_1..H_{L-1}, Z, G, row_loss).
+ * mlp_workspace_offsets.  The masked hidden gradients alternate between two
+ * buffers, starting with the first for dH_{L-1} (so after the step dH_{L-1-2k}
+ * is in the first and dH_{L-2-2k} in the second).
  * ---------------------------------------------------------------------- */
 typedef struct ge_mlp_desc {
   int32_t n_layers;     /* number of weight layers L >= 1 */
@@ -257,7 +259,8 @@ typedef struct ge_mlp_buffers {
 
 int64_t mlp_param_count(int32_t n_layers, const int64_t *dims);
 int64_t mlp_workspace_bytes(const ge_mlp_desc *desc, int64_t B);
-/* writes n_layers + 2 byte offsets: H_1 .. H_{L-1}, Z (f32), G, row_loss (f32) */
+/* writes n_layers + 4 byte offsets: H_1 .. H_{L-1}, Z (f32), G, row_loss (f32),
+ * and the two hidden-gradient buffers */
 int mlp_workspace_offsets(const ge_mlp_desc *desc, int64_t B, int64_t *offsets, int32_t n);
 int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const void *X,
                    const int32_t *labels, int64_t B, float lr, float momentum,

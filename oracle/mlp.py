@@ -57,8 +57,13 @@ def _plan(plan: str):
     raise ValueError(plan)
 
 
-def mlp_forward(params, dims, X, plan: str = "f32"):
-    """Forward pass; returns (list of stored activations [X, H1, ...], pre-activations, Z)."""
+def mlp_forward(params, dims, X, plan: str = "f32", given_H=None):
+    """Forward pass; returns (list of stored activations [X, H1, ...], pre-activations, Z).
+
+    ``given_H`` (optional list [H1, ...]) makes layer l read the given stored
+    H_{l-1} instead of the oracle's own, so each layer is checked on the
+    inputs it actually consumed.
+    """
     P = _plan(plan)
     layers = mlp_unflatten(params, dims)
     Hs, pres = [np.asarray(X, dtype=np.float64)], []
@@ -66,7 +71,8 @@ def mlp_forward(params, dims, X, plan: str = "f32"):
     for li, (W, b) in enumerate(layers):
         Wg = round_fmt(W, P["gemm_w"]) if P["gemm_w"] else W
         last = li == L - 1
-        out, pre = gemm_epilogue(Hs[-1], Wg, "NN", 1.0, b, "none" if last else "relu",
+        inp = Hs[-1] if (given_H is None or li == 0) else np.asarray(given_H[li - 1], np.float64)
+        out, pre = gemm_epilogue(inp, Wg, "NN", 1.0, b, "none" if last else "relu",
                                  out_fmt=P["logits"] if last else P["act"], pre_fmt="f64")
         pres.append(pre)
         if last:
@@ -75,7 +81,7 @@ def mlp_forward(params, dims, X, plan: str = "f32"):
 
 
 def mlp_step(params, vel, dims, X, labels, lr: float, momentum: float,
-             plan: str = "f32", mask_hint=None, tie_abs: float = 0.0):
+             plan: str = "f32", mask_hint=None, tie_abs: float = 0.0, given=None):
     """One training step; returns a dict of every stored tensor and the update.
 
     ``mask_hint``: optional list of the GPU's stored hidden activations
@@ -83,20 +89,29 @@ def mlp_step(params, vel, dims, X, labels, lr: float, momentum: float,
     zero, the ReLU-mask bit of the backward pass is taken from the hint (both
     bits are correct within the forward rounding error); the number of such
     adopted bits that differ is reported as ``mask_ties``.
+
+    ``given``: optional dict of the GPU's stored tensors -- "H" [H1, ...],
+    "Z", "G", "dH" [dH_1, ...] (dH_l is the masked gradient at H_l) -- each
+    stage then starts from the stored inputs it consumed (stage-wise check).
     """
     P = _plan(plan)
+    given = given or {}
     X = np.asarray(X, dtype=np.float64)
     B = X.shape[0]
     layers = mlp_unflatten(params, dims)
     L = len(layers)
-    Hs, pres, Z = mlp_forward(params, dims, X, plan)
+    gH = given.get("H")
+    Hs, pres, Z = mlp_forward(params, dims, X, plan, given_H=gH)
+    if gH is not None:
+        Hs = [Hs[0]] + [np.asarray(h, np.float64) for h in gH]
     grad_scale = 1.0 if P["unscaled"] else 1.0 / B
     alpha = 1.0 / B if P["unscaled"] else 1.0
-    loss, row_loss, G, argmax = softmax_xent(Z, labels, grad_scale, P["dz"])
+    Zin = np.asarray(given["Z"], np.float64) if "Z" in given else Z
+    loss, row_loss, G, argmax = softmax_xent(Zin, labels, grad_scale, P["dz"])
     grads = [None] * L
     dHs = [None] * L
     ties = 0
-    Gl = G
+    Gl = np.asarray(given["G"], np.float64) if "G" in given else G
     for li in range(L - 1, -1, -1):
         W, _ = layers[li]
         Wg = round_fmt(W, P["gemm_w"]) if P["gemm_w"] else W
@@ -114,6 +129,8 @@ def mlp_step(params, vel, dims, X, labels, lr: float, momentum: float,
             Gl, _ = gemm_epilogue(Gl, Wg, "NT", 1.0, act="relu_mask_bwd", aux=mask_src,
                                   out_fmt=P["act"])
             dHs[li - 1] = Gl
+            if "dH" in given:
+                Gl = np.asarray(given["dH"][li - 1], np.float64)
     gflat = np.concatenate([np.concatenate([dW.ravel(), db]) for dW, db in grads])
     if plan == "f64":
         vnew = momentum * np.asarray(vel, dtype=np.float64) - lr * gflat
