@@ -55,6 +55,22 @@ class MlpBuffers(C.Structure):
                 ("workspace", vp), ("workspace_bytes", i64)]
 
 
+class BlockArgs(C.Structure):
+    _fields_ = [("rows", i64), ("D", i64), ("F", i64), ("eps", f32), ("slope", f32), ("type", i32),
+                ("x", vp), ("w_up", vp), ("w_down", vp), ("dy", vp), ("y", vp), ("r", vp),
+                ("n", vp), ("u", vp), ("a", vp), ("du", vp), ("dn", vp), ("dx", vp),
+                ("dw_up", vp), ("dw_down", vp), ("workspace", vp), ("workspace_bytes", i64)]
+
+
+class GruDesc(C.Structure):
+    _fields_ = [("V", i64), ("H", i64), ("B", i64), ("T", i64), ("eps", f32)]
+
+
+class GruBuffers(C.Structure):
+    _fields_ = [("params", vp), ("grads", vp), ("velocity", vp), ("params_lowp", vp),
+                ("workspace", vp), ("workspace_bytes", i64)]
+
+
 # name -> (restype, argtypes); every function declared in include/*.h
 SIGNATURES = {
     "ge_abi_version": (i32, []),
@@ -71,11 +87,18 @@ SIGNATURES = {
     "mlp_workspace_bytes": (i64, [C.POINTER(MlpDesc), i64]),
     "mlp_workspace_offsets": (i32, [C.POINTER(MlpDesc), i64, C.POINTER(i64), i32]),
     "mlp_train_step": (i32, [C.POINTER(MlpDesc), C.POINTER(MlpBuffers), vp, vp, i64, f32, f32, vp, vp]),
-    "embedding_gather": (i32, [vp, i64, i32, vp, i64, i64, vp, i64, i32, vp]),
-    "embedding_grad": (i32, [vp, i64, vp, i64, i64, i64, f32, vp, i64, vp]),
-    "gru_gates_fwd": (i32, [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]),
-    "gru_gates_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
+    "mlp_block_workspace_bytes": (i64, [i64, i64, i64, i32]),
+    "mlp_block_fwd_bwd": (i32, [C.POINTER(BlockArgs), vp]),
+    "embedding_gather": (i32, [vp, i64, i64, i64, i32, vp, i64, vp, i64, i32, vp]),
+    "embedding_grad": (i32, [vp, i64, i32, vp, i64, i64, i64, f32, vp, i64, vp]),
+    "gru_param_count": (i64, [i64, i64]),
+    "gru_workspace_bytes": (i64, [C.POINTER(GruDesc)]),
+    "gru_workspace_offsets": (i32, [C.POINTER(GruDesc), C.POINTER(i64), i32]),
+    "gru_lm_train_step": (i32, [C.POINTER(GruDesc), C.POINTER(GruBuffers), vp, f32, f32, vp, vp]),
 }
+
+GRU_WS = ("INP", "TGT", "X16", "GI", "GH", "H16", "HS", "R", "Z", "N", "HN", "RSTD", "LOGITS", "G",
+          "ROW_LOSS", "DHN", "DH_OUT", "DGH", "DGI", "DX", "ZERO_H", "CARRY", "DH_DIR")
 
 
 def _mapped_hip_runtimes():

@@ -245,3 +245,131 @@ class MLPTrainer:
                 dH[l - 1] = view(offs[L + 2 + k], B, self.dims[l], self.storage, es)
         out["dH"] = dH
         return out
+
+
+# ------------------------------------------------------------ MLP block ------
+
+def block_workspace_bytes(rows: int, D: int, F: int, dtype=torch.bfloat16) -> int:
+    return int(lib.mlp_block_workspace_bytes(rows, D, F, dtype_code(dtype)))
+
+
+def mlp_block_fwd_bwd(x, w_up, w_down, dy, *, eps: float = 1e-6, slope: float = 0.5, out=None,
+                      workspace=None):
+    """Transformer MLP block forward + backward (see mlp_block_fwd_bwd in the header).
+
+    Returns a dict of device tensors y, r, n, u, a, du, dn, dx, dW_up, dW_down.
+    """
+    from ._lib import BlockArgs
+    R, D = x.shape
+    F = w_up.shape[1]
+    dev, t = x.device, x.dtype
+    o = out or {}
+
+    def buf(name, shape, dt):
+        if name not in o:
+            o[name] = torch.empty(shape, dtype=dt, device=dev)
+        return o[name]
+
+    for name in ("y", "n", "dx"):
+        buf(name, (R, D), t)
+    for name in ("u", "a", "du"):
+        buf(name, (R, F), t)
+    buf("r", (R,), torch.float32)
+    buf("dn", (R, D), torch.float32)
+    buf("dW_up", (D, F), torch.float32)
+    buf("dW_down", (F, D), torch.float32)
+    ws = _workspace(block_workspace_bytes(R, D, F, t), dev, workspace)
+    a = BlockArgs(R, D, F, eps, slope, dtype_code(t), x.data_ptr(), w_up.data_ptr(),
+                  w_down.data_ptr(), dy.data_ptr(), o["y"].data_ptr(), o["r"].data_ptr(),
+                  o["n"].data_ptr(), o["u"].data_ptr(), o["a"].data_ptr(), o["du"].data_ptr(),
+                  o["dn"].data_ptr(), o["dx"].data_ptr(), o["dW_up"].data_ptr(),
+                  o["dW_down"].data_ptr(), None if ws is None else ws.data_ptr(),
+                  0 if ws is None else ws.numel())
+    for tsr in (x, w_up, w_down, dy):
+        if not tsr.is_contiguous():
+            raise ValueError("mlp_block_fwd_bwd expects contiguous tensors")
+    check(lib.mlp_block_fwd_bwd(C.byref(a), _stream()), "mlp_block_fwd_bwd")
+    o["workspace"] = ws
+    return o
+
+
+# ------------------------------------------------------- GRU language model ------
+
+def embedding_gather(table, idx, *, out=None, out_dtype=None):
+    V, H = table.shape
+    n = idx.numel()
+    out = torch.empty((n, H), dtype=out_dtype or table.dtype, device=table.device) if out is None else out
+    check(lib.embedding_gather(_ptr(table), V, H, _ld(table), dtype_code(table.dtype), _ptr(idx), n,
+                               _ptr(out), _ld(out), dtype_code(out.dtype), _stream()), "embedding_gather")
+    return out
+
+
+def embedding_grad(dX, idx, V: int, alpha: float = 1.0, *, out=None):
+    n, H = dX.shape
+    out = torch.empty((V, H), dtype=torch.float32, device=dX.device) if out is None else out
+    check(lib.embedding_grad(_ptr(dX), _ld(dX), dtype_code(dX.dtype), _ptr(idx), n, V, H, alpha,
+                             _ptr(out), _ld(out), _stream()), "embedding_grad")
+    return out
+
+
+def gru_param_count(V: int, H: int) -> int:
+    return int(lib.gru_param_count(V, H))
+
+
+class GRUTrainer:
+    """Device buffers of the byte-level GRU LM and one gru_lm_train_step per call.
+
+    Flat f32 parameters [E, W_i, b_i, W_h, b_h, W_c, b_c] with an FP16
+    working copy that the update keeps in step.
+    """
+
+    def __init__(self, V: int, H: int, B: int, T: int, eps: float = 1e-6, device="cuda", params=None):
+        from ._lib import GRU_WS, GruBuffers, GruDesc
+        self.V, self.H, self.B, self.T = V, H, B, T
+        self.desc = GruDesc(V, H, B, T, eps)
+        P = gru_param_count(V, H)
+        self.P = P
+        self.params = torch.zeros(P, dtype=torch.float32, device=device)
+        if params is not None:
+            self.params.copy_(params)
+        self.grads = torch.zeros(P, dtype=torch.float32, device=device)
+        self.velocity = torch.zeros(P, dtype=torch.float32, device=device)
+        self.params_lowp = self.params.to(torch.float16)
+        nbytes = int(lib.gru_workspace_bytes(C.byref(self.desc)))
+        if nbytes < 0:
+            raise ValueError("bad GRU sizes (V <= 4096, 4 <= H <= 4096, H % 4 == 0)")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self.bufs = GruBuffers(self.params.data_ptr(), self.grads.data_ptr(), self.velocity.data_ptr(),
+                               self.params_lowp.data_ptr(), self.workspace.data_ptr(), nbytes)
+        offs = (C.c_int64 * len(GRU_WS))()
+        check(lib.gru_workspace_offsets(C.byref(self.desc), offs, len(GRU_WS)), "gru_workspace_offsets")
+        self._offs = dict(zip(GRU_WS, list(offs)))
+
+    def step(self, tokens, lr: float, momentum: float):
+        if tokens.dtype != torch.int32 or tuple(tokens.shape) != (self.B, self.T + 1):
+            raise ValueError("tokens must be int32 [B x (T+1)]")
+        check(lib.gru_lm_train_step(C.byref(self.desc), C.byref(self.bufs), _ptr(tokens), lr, momentum,
+                                    _ptr(self.loss), _stream()), "gru_lm_train_step")
+        return self.loss
+
+    def view(self, name: str):
+        """A stored tensor of the last step (rows time-major, t*B + b)."""
+        NT, H, V, B = self.B * self.T, self.H, self.V, self.B
+        shapes = {"INP": ((NT,), torch.int32), "TGT": ((NT,), torch.int32),
+                  "X16": ((NT, H), torch.float16), "GI": ((NT, 3 * H), torch.float32),
+                  "GH": ((NT, 3 * H), torch.float32), "H16": ((NT + B, H), torch.float16),
+                  "HS": ((NT, H), torch.float32), "R": ((NT, H), torch.float32),
+                  "Z": ((NT, H), torch.float32), "N": ((NT, H), torch.float32),
+                  "HN": ((NT, H), torch.float16), "RSTD": ((NT,), torch.float32),
+                  "LOGITS": ((NT, V), torch.float32), "G": ((NT, V), torch.float16),
+                  "ROW_LOSS": ((NT,), torch.float32), "DHN": ((NT, H), torch.float32),
+                  "DH_OUT": ((NT, H), torch.float32), "DGH": ((NT, 3 * H), torch.float16),
+                  "DGI": ((NT, 3 * H), torch.float16), "DX": ((NT, H), torch.float32)}
+        shape, dt = shapes[name]
+        n = 1
+        for s in shape:
+            n *= s
+        es = torch.tensor([], dtype=dt).element_size()
+        o = self._offs[name]
+        return self.workspace[o:o + n * es].view(dt).view(shape)

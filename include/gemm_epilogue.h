@@ -266,6 +266,109 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
                    const int32_t *labels, int64_t B, float lr, float momentum,
                    float *loss_out, ge_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * mlp_block_fwd_bwd -- transformer MLP block, forward and backward
+ * [MK] "What Worked": RMSNorm -> up projection -> LeakyReLU^2 -> down
+ * projection -> residual; "Credits": the activation derivative as a
+ * backward GEMM epilogue.  [CAT] "The Debugging Lesson Was Numerical": FP32
+ * normalisation statistics.  Enqueues, on `stream`:
+ *   r = 1/sqrt(mean_j x^2 + eps);  n = x r                      (RMSNorm)
+ *   u = n W_up (stored), a = (u > 0 ? u : slope u)^2            (NN, from FP32 u)
+ *   y = x + a W_down                                            (NN, residual)
+ *   du = (dy W_down^T) * (u > 0 ? 2u : 2 slope^2 u)             (NT, stored u)
+ *   dW_down = a^T dy;  dn = du W_up^T;  dW_up = n^T du          (TN, NT, TN)
+ *   dx = dy + r (dn - xh mean_j(dn xh)),  xh = x r              (RMSNorm bwd)
+ * type (GE_BF16 or GE_F16) is the storage of x, W_up [D x F], W_down [F x D],
+ * dy, and of the outputs y, n, u, a, du, dx (all row-major, contiguous);
+ * r (f32 [rows]), dn (f32 [rows x D]), dw_up (f32 [D x F]) and dw_down (f32
+ * [F x D]) are FP32.  All pointers are device memory owned by the caller;
+ * the weight gradients need mlp_block_workspace_bytes() of workspace.
+ * 1 <= D <= 4096.
+ * ---------------------------------------------------------------------- */
+typedef struct ge_block_args {
+  int64_t rows, D, F;
+  float eps, slope;
+  int32_t type;
+  const void *x, *w_up, *w_down, *dy;
+  void *y;
+  float *r;
+  void *n, *u, *a, *du;
+  float *dn;
+  void *dx;
+  float *dw_up, *dw_down;
+  void *workspace;
+  int64_t workspace_bytes;
+} ge_block_args;
+
+int64_t mlp_block_workspace_bytes(int64_t rows, int64_t D, int64_t F, int32_t type);
+int mlp_block_fwd_bwd(const ge_block_args *args, ge_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Embedding rows and their gradient (the byte-level recurrent LM).
+ * embedding_gather: out[i, :] = table[idx[i], :] for i < n; table [V x H]
+ * (type, ld_table), out [n x H] (out_type, ld_out); an index outside [0, V)
+ * yields a zero row (nothing is read for it).
+ * embedding_grad: dE[v, :] = alpha * sum over i with idx[i] == v of dX[i, :],
+ * summed in increasing i (deterministic); every row of dE [V x H] (f32,
+ * ld_de) is written, rows with no occurrence get zeros.
+ * ---------------------------------------------------------------------- */
+int embedding_gather(const void *table, int64_t V, int64_t H, int64_t ld_table, int32_t type,
+                     const int32_t *idx, int64_t n, void *out, int64_t ld_out, int32_t out_type,
+                     ge_stream_t stream);
+int embedding_grad(const void *dX, int64_t ld_dx, int32_t dx_type, const int32_t *idx, int64_t n,
+                   int64_t V, int64_t H, float alpha, float *dE, int64_t ld_de, ge_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * gru_lm_train_step -- one training step of a byte-level GRU language model
+ * [CAT] "The Work Moved Down a Layer": GEMM, GRU gates, RMSNorm, softmax
+ * cross-entropy, gradient reduction and optimizer shaders; "Keep state
+ * resident"; "The Debugging Lesson Was Numerical": recurrent state and
+ * normalisation statistics in FP32, FP16 for GEMM inputs.  The pages print no
+ * GRU equations; the cell is the standard one, gate blocks (r, z, n) along
+ * 3H, hidden bias inside the reset product, h_0 = 0:
+ *   GI = x_t W_i + b_i;  GH = h_{t-1} W_h + b_h;  r = sigmoid(GI_r + GH_r);
+ *   z = sigmoid(GI_z + GH_z);  n = tanh(GI_n + r GH_n);  h_t = (1-z) n + z h_{t-1}
+ * then hn = RMSNorm(h_t) (eps, no gain), logits = hn W_c + b_c, mean softmax
+ * cross-entropy against the next byte over all B*T positions, full
+ * backpropagation through time and one momentum update over the flat buffer
+ * [E (V x H), W_i (H x 3H), b_i (3H), W_h (H x 3H), b_h (3H), W_c (H x V),
+ * b_c (V)] (gru_param_count(V, H) floats).
+ * tokens: device int32 [B x (T+1)] (inputs t0..t_{T-1}, targets t1..t_T).
+ * params / grads / velocity: device f32; params_lowp: device f16 working
+ * copy of params, kept in step by the update (GEMMs read it).  FP16 storage:
+ * embedded inputs, the FP16 copy of h_{t-1}, hn, dZ (unscaled p - onehot),
+ * the gate gradients; everything else FP32; alpha = 1/(B*T) is applied in
+ * the weight, bias and embedding gradients.  loss_out: device f32 [1].
+ * Workspace: gru_workspace_bytes(desc); gru_workspace_offsets reports where
+ * each stored tensor lives (GE_GRU_WS_* order; rows time-major, t*B + b).
+ * Constraints: V <= 4096, 4 <= H <= 4096, H % 4 == 0.
+ * ---------------------------------------------------------------------- */
+typedef struct ge_gru_desc {
+  int64_t V, H, B, T;
+  float eps;
+} ge_gru_desc;
+
+typedef struct ge_gru_buffers {
+  float *params, *grads, *velocity;
+  void *params_lowp;
+  void *workspace;
+  int64_t workspace_bytes;
+} ge_gru_buffers;
+
+enum {
+  GE_GRU_WS_INP, GE_GRU_WS_TGT, GE_GRU_WS_X16, GE_GRU_WS_GI, GE_GRU_WS_GH, GE_GRU_WS_H16,
+  GE_GRU_WS_HS, GE_GRU_WS_R, GE_GRU_WS_Z, GE_GRU_WS_N, GE_GRU_WS_HN, GE_GRU_WS_RSTD,
+  GE_GRU_WS_LOGITS, GE_GRU_WS_G, GE_GRU_WS_ROW_LOSS, GE_GRU_WS_DHN, GE_GRU_WS_DH_OUT,
+  GE_GRU_WS_DGH, GE_GRU_WS_DGI, GE_GRU_WS_DX, GE_GRU_WS_ZERO_H, GE_GRU_WS_CARRY,
+  GE_GRU_WS_DH_DIR, GE_GRU_WS_COUNT
+};
+
+int64_t gru_param_count(int64_t V, int64_t H);
+int64_t gru_workspace_bytes(const ge_gru_desc *desc);
+int gru_workspace_offsets(const ge_gru_desc *desc, int64_t *offsets, int32_t n);
+int gru_lm_train_step(const ge_gru_desc *desc, const ge_gru_buffers *buf, const int32_t *tokens,
+                      float lr, float momentum, float *loss_out, ge_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

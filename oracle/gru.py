@@ -69,9 +69,12 @@ def gru_step(flat, vel, tokens, H: int, V: int, lr: float, momentum: float,
              eps: float = 1e-6, plan: str = "f16", given=None, update: bool = True):
     """One training step; returns a dict of the stored tensors, loss and update.
 
-    ``given``: optional GPU-stored tensors by name -- "hs" [T*B x H] (then the
-    recurrence at step t starts from the given h_{t-1}) -- so that per-step
-    checks do not inherit differences from earlier steps.
+    ``given``: optional GPU-stored tensors by name, each replacing the
+    oracle's own value wherever later stages consume it: "hs" (the recurrence
+    at step t then starts from the given h_{t-1}), "R", "Z", "N", "GH",
+    "rstd", "hn", "logits", "G", "dhn", "dh_out", "dGH" (also feeds the carry
+    into step t-1), "dGI", "dX".  Every stage is then checked on the inputs
+    it actually consumed, without inheriting differences from earlier stages.
     """
     given = given or {}
     lo = "f16" if plan == "f16" else "f64"
@@ -107,21 +110,32 @@ def gru_step(flat, vel, tokens, H: int, V: int, lr: float, momentum: float,
         hprev16[rows] = h16
         h = round_fmt(hn_, hi)
         hs[rows] = h
-    hn, rr = rmsnorm_fwd(hs, eps, y_fmt=lo, r_fmt=hi)
-    Zl, _ = gemm_epilogue(hn, Pw["W_c"], "NN", bias=P["b_c"], out_fmt=hi)
-    loss, row_loss, G, argmax = softmax_xent(Zl, tgt, 1.0, lo)
+    def use(name, own):
+        return np.asarray(given[name], dtype=np.float64) if name in given else own
+
+    hs_u = use("hs", hs)
+    hprev16 = np.concatenate([np.zeros((Bn, H)), round_fmt(hs_u[:(T - 1) * Bn], lo)])
+    R_u, Z_u, N_u = use("R", R), use("Z", Zg), use("N", Nn)
+    GHn_u = use("GH", None)[:, 2 * H:] if "GH" in given else GHn
+    hn, rr = rmsnorm_fwd(hs_u, eps, y_fmt=lo, r_fmt=hi)
+    hn_u, rr_u = use("hn", hn), use("rstd", rr)
+    Zl, _ = gemm_epilogue(hn_u, Pw["W_c"], "NN", bias=P["b_c"], out_fmt=hi)
+    loss, row_loss, G, argmax = softmax_xent(use("logits", Zl), tgt, 1.0, lo)
+    G_u = use("G", G)
     alpha = 1.0 / (T * Bn)
-    dW_c, _ = gemm_epilogue(hn, G, "TN", alpha, out_fmt=hi)
-    db_c = colsum(G, alpha, hi)
-    dhn, _ = gemm_epilogue(G, Pw["W_c"], "NT", out_fmt=hi)
-    dh_out, _ = rmsnorm_bwd(hs, rr, dhn, dx_fmt=hi)
+    dW_c, _ = gemm_epilogue(hn_u, G_u, "TN", alpha, out_fmt=hi)
+    db_c = colsum(G_u, alpha, hi)
+    dhn, _ = gemm_epilogue(G_u, Pw["W_c"], "NT", out_fmt=hi)
+    dh_out, _ = rmsnorm_bwd(hs_u, rr_u, use("dhn", dhn), dx_fmt=hi)
+    dh_out_u = use("dh_out", dh_out)
     dGH = np.zeros((T * Bn, 3 * H)); dGI = np.zeros((T * Bn, 3 * H))
+    gdGH = given.get("dGH")
     carry = np.zeros((Bn, H))
     for t in range(T - 1, -1, -1):
         rows = slice(t * Bn, (t + 1) * Bn)
-        r, z, n, ghn = R[rows], Zg[rows], Nn[rows], GHn[rows]
-        hp = hs[(t - 1) * Bn:t * Bn] if t > 0 else np.zeros((Bn, H))
-        dh = dh_out[rows] + carry
+        r, z, n, ghn = R_u[rows], Z_u[rows], N_u[rows], GHn_u[rows]
+        hp = hs_u[(t - 1) * Bn:t * Bn] if t > 0 else np.zeros((Bn, H))
+        dh = dh_out_u[rows] + carry
         dn = dh * (1.0 - z)
         dz = dh * (hp - n)
         dh_dir = round_fmt(dh * z, hi)
@@ -131,14 +145,16 @@ def gru_step(flat, vel, tokens, H: int, V: int, lr: float, momentum: float,
         dgz = dz * z * (1.0 - z)
         dGH[rows] = round_fmt(np.concatenate([dgr, dgz, dnh * r], axis=1), lo)
         dGI[rows] = round_fmt(np.concatenate([dgr, dgz, dnh], axis=1), lo)
-        carry, _ = gemm_epilogue(dGH[rows], Pw["W_h"], "NT", residual=dh_dir, out_fmt=hi)
-    dW_h, _ = gemm_epilogue(hprev16, dGH, "TN", alpha, out_fmt=hi)
-    dW_i, _ = gemm_epilogue(X, dGI, "TN", alpha, out_fmt=hi)
-    db_h = colsum(dGH, alpha, hi)
-    db_i = colsum(dGI, alpha, hi)
-    dX, _ = gemm_epilogue(dGI, Pw["W_i"], "NT", out_fmt=hi)
+        src = dGH[rows] if gdGH is None else np.asarray(gdGH[rows], dtype=np.float64)
+        carry, _ = gemm_epilogue(src, Pw["W_h"], "NT", residual=dh_dir, out_fmt=hi)
+    dGH_u, dGI_u = use("dGH", dGH), use("dGI", dGI)
+    dW_h, _ = gemm_epilogue(hprev16, dGH_u, "TN", alpha, out_fmt=hi)
+    dW_i, _ = gemm_epilogue(X, dGI_u, "TN", alpha, out_fmt=hi)
+    db_h = colsum(dGH_u, alpha, hi)
+    db_i = colsum(dGI_u, alpha, hi)
+    dX, _ = gemm_epilogue(dGI_u, Pw["W_i"], "NT", out_fmt=hi)
     dE = np.zeros((V, H))
-    np.add.at(dE, inp, dX)
+    np.add.at(dE, inp, use("dX", dX))
     dE = round_fmt(alpha * dE, hi)
     grads = {"E": dE, "W_i": dW_i, "b_i": db_i, "W_h": dW_h, "b_h": db_h,
              "W_c": dW_c, "b_c": db_c}

@@ -1,0 +1,88 @@
+"""GPU parity of mlp_block_fwd_bwd (transformer MLP block, BF16 storage)."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from parity import TOL_LOWP, assert_parity, compare
+
+pytestmark = pytest.mark.gpu
+TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def ge():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gemm_epilogue_amd
+    return gemm_epilogue_amd
+
+
+def dev(x, fmt):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(TD[fmt]).cuda()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+STORED = {"n": "bf16", "u": "bf16", "a": "bf16", "y": "bf16", "du": "bf16", "dx": "bf16",
+          "r": "f32", "dn": "f32", "dW_up": "f32", "dW_down": "f32"}
+
+
+@pytest.mark.parametrize("R,D,F", [(1, 8, 12), (77, 64, 96), (1000, 512, 1536), (4096, 512, 1536)])
+def test_block_stagewise(ge, R, D, F):
+    fmt = "bf16"
+    x, wu, wd, dy = datagen.block_inputs(R, D, F, seed=R)
+    o = ge.mlp_block_fwd_bwd(dev(x, fmt), dev(wu, fmt), dev(wd, fmt), dev(dy, fmt), eps=1e-6, slope=0.5)
+    torch.cuda.synchronize()
+    got = {k: host(o[k]) for k in STORED}
+    # every stage against the oracle applied to the GPU's stored inputs of that stage
+    given = {k: got[k] for k in ("r", "n", "u", "a", "du", "dn")}
+    ref = oracle.block_fwd_bwd(x, wu, wd, dy, eps=1e-6, slope=0.5, fmt=fmt, given=given)
+    for k, f in STORED.items():
+        assert_parity(got[k], ref[k], TOL_LOWP, f, f"{k} R={R}")
+    # end to end (oracle's own intermediates): reported, cosine-bounded
+    e2e = oracle.block_fwd_bwd(x, wu, wd, dy, eps=1e-6, slope=0.5, fmt=fmt)
+    for k in ("y", "dx", "dW_up", "dW_down"):
+        c = compare(got[k], e2e[k], TOL_LOWP, STORED[k])
+        print(f"R={R} {k}: end-to-end cos {c['cos']:.8f}, fails {c['fails']}/{c['n']}")
+        assert c["cos"] > 0.9999, k
+
+
+def test_block_full_size_sampled(ge):
+    """98,304 rows (48 x 2048 tokens) x 512 x 1536, BF16: sampled rows of every
+    row-local output, sampled elements of both weight gradients (each a sum over
+    all 98,304 rows), checked on the GPU's stored inputs."""
+    R, D, F = 98304, 512, 1536
+    fmt = "bf16"
+    x, wu, wd, dy = datagen.block_inputs(R, D, F, seed=3)
+    o = ge.mlp_block_fwd_bwd(dev(x, fmt), dev(wu, fmt), dev(wd, fmt), dev(dy, fmt), eps=1e-6, slope=0.5)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(7)
+    rows = np.sort(g.choice(R, 256, replace=False))
+    rows[-1] = R - 1
+    sub = {k: host(o[k][torch.from_numpy(rows).cuda()]) for k in ("n", "u", "a", "y", "du", "dn", "dx")}
+    sub["r"] = host(o["r"])[rows]
+    given = {k: sub[k] for k in ("r", "n", "u", "a", "du", "dn")}
+    ref = oracle.block_fwd_bwd(x[rows], wu, wd, dy[rows], eps=1e-6, fmt=fmt, given=given)
+    for k in ("r", "n", "u", "a", "y", "du", "dn", "dx"):
+        assert_parity(sub[k], ref[k], TOL_LOWP, STORED[k], f"full {k}")
+    # weight gradients: sampled output elements, full K = 98,304 reduction on stored a, n, du, dy
+    a_all, n_all, du_all = host(o["a"]), host(o["n"]), host(o["du"])
+    fi = g.choice(F, 48, replace=False)
+    di = g.choice(D, 48, replace=False)
+    ref_dwd = oracle.gemm_epilogue(a_all[:, fi], dy[:, di], "TN", out_fmt="f32")[0]
+    assert_parity(host(o["dW_down"])[np.ix_(fi, di)], ref_dwd, TOL_LOWP, "f32", "dW_down")
+    ref_dwu = oracle.gemm_epilogue(n_all[:, di], du_all[:, fi], "TN", out_fmt="f32")[0]
+    assert_parity(host(o["dW_up"])[np.ix_(di, fi)], ref_dwu, TOL_LOWP, "f32", "dW_up")
+
+
+def test_block_zero_down_projection(ge):
+    x, wu, wd, dy = datagen.block_inputs(300, 64, 96, seed=11)
+    o = ge.mlp_block_fwd_bwd(dev(x, "bf16"), dev(wu, "bf16"), torch.zeros((96, 64), dtype=torch.bfloat16,
+                                                                          device="cuda"), dev(dy, "bf16"))
+    np.testing.assert_array_equal(host(o["y"]), x)
+    np.testing.assert_array_equal(host(o["du"]), 0.0)
+    np.testing.assert_array_equal(host(o["dW_up"]), 0.0)
+    np.testing.assert_array_equal(host(o["dx"]), dy)

@@ -1,0 +1,105 @@
+"""GPU parity of the byte-level GRU LM step (gru_lm_train_step) and the
+embedding entry points, against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from parity import TOL_LOSS, TOL_LOWP, assert_parity, compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ge():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gemm_epilogue_amd
+    return gemm_epilogue_amd
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# GPU workspace name -> (oracle name, storage format)
+STAGES = {"GI": ("GI", "f32"), "HS": ("hs", "f32"), "R": ("R", "f32"), "Z": ("Zg", "f32"),
+          "N": ("N", "f32"), "HN": ("hn", "f16"), "RSTD": ("rstd", "f32"), "LOGITS": ("logits", "f32"),
+          "G": ("G", "f16"), "DHN": ("dhn", "f32"), "DH_OUT": ("dh_out", "f32"), "DGH": ("dGH", "f16"),
+          "DGI": ("dGI", "f16"), "DX": ("dX", "f32")}
+GIVEN = {"HS": "hs", "R": "R", "Z": "Z", "N": "N", "GH": "GH", "RSTD": "rstd", "HN": "hn",
+         "LOGITS": "logits", "G": "G", "DHN": "dhn", "DH_OUT": "dh_out", "DGH": "dGH", "DGI": "dGI",
+         "DX": "dX"}
+
+
+def _run_and_check(ge, V, H, B, T, lr, mu, params, what, steps=1):
+    tok = datagen.zipf_tokens(B, T + 1, seed=B + T, vocab=V)
+    flat = datagen.representable(params, "f32")
+    tr = ge.GRUTrainer(V, H, B, T, eps=1e-6, params=torch.from_numpy(flat).float().cuda())
+    vel = np.zeros_like(flat)
+    for s in range(steps):
+        w0, v0 = host(tr.params), host(tr.velocity)
+        tr.step(torch.from_numpy(tok).cuda(), lr, mu)
+        torch.cuda.synchronize()
+        got = {k: host(tr.view(k)) for k in list(STAGES) + ["GH"]}
+        given = {GIVEN[k]: got[k] for k in GIVEN}
+        print(f"{what} step {s}: oracle", flush=True)
+        ref = oracle.gru_step(w0, v0, tok, H, V, lr, mu, eps=1e-6, plan="f16", given=given)
+        loss = host(tr.loss)[0]
+        assert abs(loss - ref["loss"]) <= TOL_LOSS * abs(ref["loss"]), (what, loss, ref["loss"])
+        for k, (rk, fmt) in STAGES.items():
+            assert_parity(got[k], ref[rk], TOL_LOWP, fmt, f"{what} {k}")
+        assert_parity(host(tr.grads), ref["grads"], TOL_LOWP, "f32", f"{what} grads")
+        assert_parity(host(tr.params), ref["params"], TOL_LOWP, "f32", f"{what} params")
+        np.testing.assert_array_equal(host(tr.params_lowp), oracle.round_fmt(host(tr.params), "f16"))
+        # end to end from the pre-step state (oracle's own intermediates): reported
+        e2e = oracle.gru_step(w0, v0, tok, H, V, lr, mu, eps=1e-6, plan="f16")
+        rl = abs(loss - e2e["loss"]) / e2e["loss"]
+        c = compare(host(tr.grads), e2e["grads"], TOL_LOWP, "f32")
+        print(f"{what} step {s}: end-to-end loss rel diff {rl:.2e}, grads cos {c['cos']:.8f}")
+        assert rl < 1e-3 and c["cos"] > 0.9999
+    return tr
+
+
+def test_gru_small_ragged(ge):
+    V, H, B, T = 100, 68, 3, 7
+    p = oracle.gru_flatten(datagen.gru_params(H, V))
+    _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, "small", steps=2)
+
+
+def test_gru_full_size(ge):
+    """Byte vocabulary 256, hidden 1024, batch 64, sequence 128, lr 0.01, momentum 0.9."""
+    V, H, B, T = 256, 1024, 64, 128
+    p = oracle.gru_flatten(datagen.gru_params(H, V))
+    _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, "cfg4")
+
+
+def test_gru_zero_weights_ln256(ge):
+    V, H, B, T = 256, 64, 4, 9
+    tr = ge.GRUTrainer(V, H, B, T)
+    tok = datagen.zipf_tokens(B, T + 1, seed=5)
+    tr.step(torch.from_numpy(tok).cuda(), 0.0, 0.0)
+    assert abs(host(tr.loss)[0] - math.log(256)) <= 1e-6 * math.log(256)
+    assert torch.all(tr.view("HS") == 0)
+
+
+def test_embedding_gather_and_grad(ge):
+    V, H, n = 37, 130, 1000
+    E = datagen.normal((V, H), 1.0, seed=1, fmt="f16")
+    idx = datagen.rng(2, "tokens").integers(-2, V + 2, size=n).astype(np.int32)   # some out of range
+    tE = torch.from_numpy(E).half().cuda()
+    ti = torch.from_numpy(idx).cuda()
+    out = ge.embedding_gather(tE, ti)
+    ok = (idx >= 0) & (idx < V)
+    ref = np.where(ok[:, None], E[np.clip(idx, 0, V - 1)], 0.0)
+    np.testing.assert_array_equal(host(out), ref)
+    dX = datagen.normal((n, H), 1.0, seed=3)
+    vi = np.clip(idx, 0, V - 1).astype(np.int32)
+    g = ge.embedding_grad(torch.from_numpy(dX).float().cuda(), torch.from_numpy(vi).cuda(), V, 0.5)
+    dE = np.zeros((V, H))
+    np.add.at(dE, vi, dX)
+    assert_parity(host(g), oracle.round_fmt(0.5 * dE, "f32"), 1e-4, "f32", "dE")
+    g2 = ge.embedding_grad(torch.from_numpy(dX).float().cuda(), torch.from_numpy(vi).cuda(), V, 0.5)
+    assert torch.equal(g, g2)
