@@ -65,24 +65,55 @@ struct GemmParams {
   EpiParams ep;
 };
 
-// Epilogue for four consecutive columns n..n+3 of row m (FP32 values v).
+// Epilogue for four consecutive columns n..n+3 of row m, in three steps so a
+// caller can batch the memory accesses of several rows: the bias of the
+// column group (loaded once per thread), the per-element inputs (aux for the
+// derivative epilogues, residual), then the arithmetic and the store.
 // `fast`: the four columns are inside the matrix and every access is aligned.
-__device__ __forceinline__ void epilogue4(const EpiParams &e, int m, int n, f32x4 acc, bool fast) {
+__device__ __forceinline__ void epi_bias(const EpiParams &e, int n, bool fast, float b[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = 0.f;
+  if (!e.bias || n >= e.N) return;
+  if ((fast || n + 3 < e.N) && e.bias_vec) {
+    const f32x4 x = *(const f32x4 *)(e.bias + n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = x[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = (n + j < e.N) ? e.bias[n + j] : 0.f;
+  }
+}
+
+__device__ __forceinline__ void epi_fetch(const EpiParams &e, int m, int n, bool fast, float a[4], float r[4]) {
   if (!fast && (m >= e.M || n >= e.N)) return;
   const bool full = fast || (n + 3) < e.N;
-  float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-  float b[4] = {0.f, 0.f, 0.f, 0.f};
-  if (e.bias) {
-    if (full && e.bias_vec) {
-      f32x4 x = *(const f32x4 *)(e.bias + n);
-      b[0] = x[0]; b[1] = x[1]; b[2] = x[2]; b[3] = x[3];
+  if (e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD) {
+    if (full) {
+      load4_any(e.aux, (int64_t)m * e.ld_aux + n, e.aux_type, e.aux_vec, a);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = (n + j < e.N) ? e.bias[n + j] : 0.f;
+      for (int j = 0; j < 4; ++j)
+        a[j] = (n + j < e.N) ? load_any(e.aux, (int64_t)m * e.ld_aux + n + j, e.aux_type) : 0.f;
     }
   }
+  if (e.res) {
+    if (full) {
+      load4_any(e.res, (int64_t)m * e.ld_res + n, e.res_type, e.res_vec, r);
+    } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = e.alpha * v[j] + b[j];
+      for (int j = 0; j < 4; ++j)
+        r[j] = (n + j < e.N) ? load_any(e.res, (int64_t)m * e.ld_res + n + j, e.res_type) : 0.f;
+    }
+  }
+}
+
+__device__ __forceinline__ void epi_apply(const EpiParams &e, int m, int n, f32x4 acc, const float b[4],
+                                          const float a[4], const float r[4], bool fast) {
+  if (!fast && (m >= e.M || n >= e.N)) return;
+  const bool full = fast || (n + 3) < e.N;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = e.alpha * acc[j] + b[j];
   if (e.pre) {
     if (full) {
       store4_any(e.pre, (int64_t)m * e.ld_pre + n, e.pre_type, e.pre_vec, v);
@@ -101,33 +132,15 @@ __device__ __forceinline__ void epilogue4(const EpiParams &e, int m, int n, f32x
       const float t = v[j] > 0.f ? v[j] : e.slope * v[j];
       v[j] = t * t;
     }
-  } else if (e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD) {
-    float a[4];
-    if (full) {
-      load4_any(e.aux, (int64_t)m * e.ld_aux + n, e.aux_type, e.aux_vec, a);
-    } else {
+  } else if (e.act == GE_ACT_RELU_MASK_BWD) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        a[j] = (n + j < e.N) ? load_any(e.aux, (int64_t)m * e.ld_aux + n + j, e.aux_type) : 0.f;
-    }
-    if (e.act == GE_ACT_RELU_MASK_BWD) {
+    for (int j = 0; j < 4; ++j) v[j] = a[j] > 0.f ? v[j] : 0.f;
+  } else if (e.act == GE_ACT_LRELU_SQ_BWD) {
+    const float s2 = 2.f * e.slope * e.slope;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = a[j] > 0.f ? v[j] : 0.f;
-    } else {
-      const float s2 = 2.f * e.slope * e.slope;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] *= (a[j] > 0.f ? 2.f * a[j] : s2 * a[j]);
-    }
+    for (int j = 0; j < 4; ++j) v[j] *= (a[j] > 0.f ? 2.f * a[j] : s2 * a[j]);
   }
   if (e.res) {
-    float r[4];
-    if (full) {
-      load4_any(e.res, (int64_t)m * e.ld_res + n, e.res_type, e.res_vec, r);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        r[j] = (n + j < e.N) ? load_any(e.res, (int64_t)m * e.ld_res + n + j, e.res_type) : 0.f;
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] += r[j];
   }
@@ -180,6 +193,13 @@ template <typename T> __device__ __forceinline__ uint32_t bits_of(T x) {
   else return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
+// ---- LDS tile layout ---------------------------------------------------------
+// Tile rows are 128 bytes (eight 16-byte chunks) with no padding; chunk q of
+// row r is stored at chunk q ^ ((r >> 1) & 7).  Measured on gfx950, the MFMA
+// fragment read (16 consecutive rows, one chunk) then runs conflict-free,
+// where a 16-byte row pad costs two-way bank conflicts.
+__device__ __forceinline__ int lds_chunk(int row, int q) { return q ^ ((row >> 1) & 7); }
+
 // ---- tile loaders ------------------------------------------------------------
 // k-contiguous source: R rows (m or n) x BK, each row contiguous along k.
 // Thread t moves vectors v = t + i*NT: row v / VPR, 16-byte chunk v % VPR.
@@ -221,7 +241,8 @@ template <typename T, int R, int BK, int NT> struct LoaderKC {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = tid + i * NT;
-      *(u32x4 *)(s + (v / VPR) * stride + (v % VPR) * VEC) = r[i];
+      const int row = v / VPR;
+      *(u32x4 *)(s + row * stride + lds_chunk(row, v % VPR) * VEC) = r[i];
     }
   }
 };
@@ -279,14 +300,19 @@ template <typename T, int R, int BK, int NT> struct LoaderMC {
         if constexpr (sizeof(T) == 4) w[q] = elem_bits<T>(x[q], e);
         else w[q] = elem_bits<T>(x[2 * q], e) | (elem_bits<T>(x[2 * q + 1], e) << 16);
       }
-      uint32_t *dst = (uint32_t *)(s + (rv * VEC + e) * stride + kg * KB);
+      // bytes [b, b + 4W) of tile row `row`; pieces of at most 16 bytes never
+      // straddle a 16-byte chunk, so each is placed by its chunk's swizzle
+      const int row = rv * VEC + e;
+      const int b = kg * KB * (int)sizeof(T);
+      char *rbase = (char *)(s + row * stride);
       if constexpr (W == 1) {
-        dst[0] = w[0];
+        *(uint32_t *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = w[0];
       } else if constexpr (W == 2) {
-        *(u32x2 *)dst = u32x2{w[0], w[1]};
+        *(u32x2 *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = u32x2{w[0], w[1]};
       } else {
 #pragma unroll
-        for (int q = 0; q < W; q += 4) *(u32x4 *)(dst + q) = u32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
+        for (int q = 0; q < W; q += 4)
+          *(u32x4 *)(rbase + lds_chunk(row, (b >> 4) + q / 4) * 16) = u32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
       }
     }
   }
@@ -302,11 +328,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
   constexpr int NT = 64 * WGM * WGN;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KCH = 4 * VEC;  // k covered by one 16-byte-per-lane fragment
-  constexpr int STRIDE = BK + VEC;
+  constexpr int STRIDE = BK;  // 128-byte rows, 16-byte chunks XOR-swizzled by row
+  static_assert(BK * sizeof(T) == 128, "the LDS swizzle assumes 128-byte tile rows");
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr bool A_KC = (LAYOUT != GE_TN);
   constexpr bool B_KC = (LAYOUT == GE_NT);
+  constexpr bool PING_PONG = (WGM == 2 && WGN * WGM == 8);
   static_assert(BK % KCH == 0, "BK must hold whole fragments");
   typedef typename Frag<T>::V V;
 
@@ -316,9 +344,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
   constexpr int NPASS = BM >= 256 ? 2 : 1;  // row passes of the staged epilogue
   constexpr int RP = BM / NPASS;
   constexpr int CSTRIDE = BN + 4;  // floats per staged row (16-byte pad)
-  static_assert(RP * CSTRIDE * 4 <= OPER_BYTES, "staged tile must fit in the operand buffers");
+  constexpr int STAGE_BYTES = RP * CSTRIDE * 4;
+  constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
+  static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
   static_assert(BM / WGM <= RP && RP % (BM / WGM) == 0, "a wave's rows must fall in one pass");
-  __shared__ __attribute__((aligned(16))) char smem[OPER_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
   T(*sA)[BM * STRIDE] = (T(*)[BM * STRIDE])smem;
   T(*sB)[BN * STRIDE] = (T(*)[BN * STRIDE])(smem + 2 * BM * STRIDE * sizeof(T));
 
@@ -347,56 +377,137 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
   const T *__restrict__ Ap = (const T *)p.A;
   const T *__restrict__ Bp = (const T *)p.B;
 
-  Loader<T, A_KC, BM, BK, NT> la;
-  Loader<T, B_KC, BN, BK, NT> lb;
-
-  auto load_tile = [&](int kt) {
-    if (interior && kt < nk_full) {
-      la.load_fast(Ap, p.lda, bm0, kt * BK, tid);
-      lb.load_fast(Bp, p.ldb, bn0, kt * BK, tid);
-    } else {
-      la.load_checked(Ap, p.lda, bm0, p.M, kt * BK, p.K, p.a_vec, tid);
-      lb.load_checked(Bp, p.ldb, bn0, p.N, kt * BK, p.K, p.b_vec, tid);
-    }
-  };
-
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (kt0 < kt1) {
-    load_tile(kt0);
-    la.store(sA[0], STRIDE, tid);
-    lb.store(sB[0], STRIDE, tid);
-    __syncthreads();
-  }
-  const int arow = (wm0 + (lane & 15)) * STRIDE + (lane >> 4) * VEC;
-  const int brow = (wn0 + (lane & 15)) * STRIDE + (lane >> 4) * VEC;
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) load_tile(kt + 1);
-    const T *a_s = sA[cur] + arow;
-    const T *b_s = sB[cur] + brow;
+  // lane reads tile row (block + lane % 16) at 16-byte chunk 4c + lane / 16;
+  // rows of a fragment start at multiples of 16, so the swizzle depends on
+  // the lane only
+  constexpr int NCH = BK / KCH;
+  const int arow = (wm0 + (lane & 15)) * STRIDE;
+  const int brow = (wn0 + (lane & 15)) * STRIDE;
+  int koff[NCH];
 #pragma unroll
-    for (int c = 0; c < BK / KCH; ++c) {
-      V af[FM], bf[FN];
+  for (int c = 0; c < NCH; ++c) koff[c] = lds_chunk(lane & 15, 4 * c + (lane >> 4)) * VEC;
+
+  // MFMAs over one LDS buffer.  Software-pipelined fragment reads: the k-tile
+  // is a sequence of S = NC*FM A fragments (chunk c, row block i); the read of
+  // fragment s+2 is issued before the MFMAs of fragment s, and the B fragments
+  // of chunk c+1 halfway through chunk c, so each LDS read has MFMA work in
+  // flight to hide its latency.  Scheduling barriers keep that order.
+  auto compute = [&](int buf) {
+    const T *a_s = sA[buf] + arow;
+    const T *b_s = sB[buf] + brow;
+    constexpr int NC = BK / KCH;
+    constexpr int S = NC * FM;
+    V af[S], bf[NC][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *(const V *)(a_s + i * 16 * STRIDE + c * KCH);
+    for (int j = 0; j < FN; ++j) bf[0][j] = *(const V *)(b_s + j * 16 * STRIDE + koff[0]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = *(const V *)(b_s + j * 16 * STRIDE + c * KCH);
+    for (int s = 0; s < 2 && s < S; ++s)
+      af[s] = *(const V *)(a_s + (s % FM) * 16 * STRIDE + koff[s / FM]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int s = 0; s < S; ++s) {
+      const int c = s / FM, i = s % FM;
+      if (s + 2 < S) af[s + 2] = *(const V *)(a_s + ((s + 2) % FM) * 16 * STRIDE + koff[(s + 2) / FM]);
+      if (i == FM / 2 && c + 1 < NC) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = Frag<T>::mma(bf[j], af[i], acc[i][j]);
+        for (int j = 0; j < FN; ++j) bf[c + 1][j] = *(const V *)(b_s + j * 16 * STRIDE + koff[c + 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = Frag<T>::mma(bf[c][j], af[s], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      la.store(sA[cur ^ 1], STRIDE, tid);
-      lb.store(sB[cur ^ 1], STRIDE, tid);
+  };
+
+  if constexpr (PING_PONG) {
+    // Two wave groups (rows 0..BM/2 and BM/2..BM of the tile; one wave of
+    // each group per SIMD) alternate: while one group multiplies tile k the
+    // other stores its half of tile k+1 (loaded one iteration earlier) into
+    // the other LDS buffer and issues the global loads of its half of tile
+    // k+2.  So every SIMD always has one wave issuing MFMAs, and each global
+    // load has a whole iteration to arrive.
+    const int g = wave / WGN;
+    const int gt = tid % (NT / 2);
+    Loader<T, A_KC, BM / 2, BK, NT / 2> la;
+    Loader<T, B_KC, BN / 2, BK, NT / 2> lb;
+    const int ar0 = bm0 + g * (BM / 2), br0 = bn0 + g * (BN / 2);
+    auto load_half = [&](int kt) {
+      if (interior && kt < nk_full) {
+        la.load_fast(Ap, p.lda, ar0, kt * BK, gt);
+        lb.load_fast(Bp, p.ldb, br0, kt * BK, gt);
+      } else {
+        la.load_checked(Ap, p.lda, ar0, p.M, kt * BK, p.K, p.a_vec, gt);
+        lb.load_checked(Bp, p.ldb, br0, p.N, kt * BK, p.K, p.b_vec, gt);
+      }
+    };
+    auto store_half = [&](int buf) {
+      la.store(sA[buf] + g * (BM / 2) * STRIDE, STRIDE, gt);
+      lb.store(sB[buf] + g * (BN / 2) * STRIDE, STRIDE, gt);
+    };
+    auto memory_phase = [&](int kt, int buf) {
+      if (kt + 1 < kt1) {
+        store_half(buf ^ 1);
+        if (kt + 2 < kt1) load_half(kt + 2);
+      }
+    };
+    if (kt0 < kt1) {
+      load_half(kt0);
+      store_half(0);
+      if (kt0 + 1 < kt1) load_half(kt0 + 1);
+      __syncthreads();
     }
-    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int buf = (kt - kt0) & 1;
+      if (g == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        compute(buf);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        memory_phase(kt, buf);
+      }
+      __syncthreads();
+      if (g == 1) {
+        __builtin_amdgcn_s_setprio(1);
+        compute(buf);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        memory_phase(kt, buf);
+      }
+      __syncthreads();
+    }
+  } else {
+    Loader<T, A_KC, BM, BK, NT> la;
+    Loader<T, B_KC, BN, BK, NT> lb;
+    auto load_tile = [&](int kt) {
+      if (interior && kt < nk_full) {
+        la.load_fast(Ap, p.lda, bm0, kt * BK, tid);
+        lb.load_fast(Bp, p.ldb, bn0, kt * BK, tid);
+      } else {
+        la.load_checked(Ap, p.lda, bm0, p.M, kt * BK, p.K, p.a_vec, tid);
+        lb.load_checked(Bp, p.ldb, bn0, p.N, kt * BK, p.K, p.b_vec, tid);
+      }
+    };
+    if (kt0 < kt1) {
+      load_tile(kt0);
+      la.store(sA[0], STRIDE, tid);
+      lb.store(sB[0], STRIDE, tid);
+      __syncthreads();
+    }
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      const bool more = kt + 1 < kt1;
+      if (more) load_tile(kt + 1);
+      compute(cur);
+      if (more) {
+        la.store(sA[cur ^ 1], STRIDE, tid);
+        lb.store(sB[cur ^ 1], STRIDE, tid);
+      }
+      __syncthreads();
+    }
   }
 
   // Epilogue: the lane owning C[m][n..n+3] of each 16x16 fragment writes it
@@ -408,6 +519,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
   float *cs = (float *)smem;
   float *part = p.splits > 1 ? p.partial + (int64_t)blockIdx.z * p.M * p.N : nullptr;
   const bool pvec = (p.N & 3) == 0;
+  // each thread owns one group of four columns and rows r0, r0 + RS, ...
+  constexpr int CG = BN / 4;
+  static_assert(NT % CG == 0, "threads must tile whole staged rows");
+  constexpr int RS = NT / CG;
+  constexpr int RPT = RP / RS;
+  // rows whose loads are issued together (fewer while a second pass still
+  // holds its accumulators in registers)
+  constexpr int EU = NPASS > 1 ? 2 : (RPT >= 4 ? 4 : RPT);
+  static_assert(RPT % EU == 0, "rows per thread must split into batches");
+  const int cg = tid % CG, r0 = tid / CG;
+  const int n = bn0 + cg * 4;
+  float bias[4];
+  epi_bias(e, n, fast, bias);
   for (int pass = 0; pass < NPASS; ++pass) {
     if (wm0 / RP == pass) {
 #pragma unroll
@@ -420,20 +544,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
         }
     }
     __syncthreads();
-    for (int g = tid; g < RP * (BN / 4); g += NT) {
-      const int r = g / (BN / 4), c = (g % (BN / 4)) * 4;
-      const f32x4 v = *(const f32x4 *)(cs + r * CSTRIDE + c);
-      const int m = bm0 + pass * RP + r, n = bn0 + c;
-      if (part == nullptr) {
-        epilogue4(e, m, n, v, fast);
-      } else if (m < p.M && n < p.N) {
-        float *dst = part + (int64_t)m * p.N + n;
-        if (pvec && n + 3 < p.N) {
-          *(f32x4 *)dst = v;
-        } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < p.N) dst[q] = v[q];
+    for (int q0 = 0; q0 < RPT; q0 += EU) {
+      f32x4 v[EU];
+      float a[EU][4], r[EU][4];
+#pragma unroll
+      for (int u = 0; u < EU; ++u) {
+        const int rr = r0 + (q0 + u) * RS;
+        v[u] = *(const f32x4 *)(cs + rr * CSTRIDE + cg * 4);
+        if (part == nullptr) epi_fetch(e, bm0 + pass * RP + rr, n, fast, a[u], r[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < EU; ++u) {
+        const int m = bm0 + pass * RP + r0 + (q0 + u) * RS;
+        if (part == nullptr) {
+          epi_apply(e, m, n, v[u], bias, a[u], r[u], fast);
+        } else if (m < p.M && n < p.N) {
+          float *dst = part + (int64_t)m * p.N + n;
+          if (pvec && n + 3 < p.N) {
+            *(f32x4 *)dst = v[u];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q < p.N) dst[q] = v[u][q];
+          }
         }
       }
     }
@@ -461,7 +595,10 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p) {
         if (n + q < p.N) v[q] += src[s * mn + q];
     }
   }
-  epilogue4(p.ep, m, n, v, false);
+  float b[4], a[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f};
+  epi_bias(p.ep, n, false, b);
+  epi_fetch(p.ep, m, n, false, a, r);
+  epi_apply(p.ep, m, n, v, b, a, r, false);
 }
 
 // ---- host launcher --------------------------------------------------------------
