@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm_epilogue.so")
-SOURCES = ["abi.cpp", "train.cpp", "block.cpp", "gru.cpp", "gemm.hip", "rowops.hip", "seq.hip"]
+SOURCES = ["abi.cpp", "train.cpp", "block.cpp", "gru.cpp", "gemm.hip", "gemm_f16.hip", "gemm_bf16.hip",
+           "gemm_f32.hip", "rowops.hip", "seq.hip"]
 ARCH = "gfx950"
 
 

@@ -1,579 +1,10 @@
-// MFMA GEMM with a fused FP32 epilogue, for gfx950 (CDNA4, wave64).
-//
-// C = act(alpha * op(A) op(B) + bias) [+ residual], layouts NN / NT / TN.
-// Bias and activation are applied to the FP32 accumulator and the value is
-// converted once at the final store ("The Work Moved Down a Layer", section
-// "The Debugging Lesson Was Numerical"; "Capstone 5: train a network with your
-// CUDA kernels", section "Read the worked reference").  The backward GEMMs of
-// "Capstone 5", section "Work through the backward pass" (dW = X^T dH,
-// dX = dH W^T, dH masked by H > 0) are the TN / NT layouts and the *_BWD
-// epilogues.
-//
-// Design (ours, not the pages'): a block of 4 wavefronts computes a BM x BN
-// tile (256x256, 128x128 or 64x64 by problem size); A and B tiles of BK along
-// k are staged through LDS, double-buffered, always stored k-contiguous
-// ([row][k], rows padded by 16 bytes) so each MFMA fragment is one 16-byte
-// LDS read per lane and the 16 lanes that read one fragment hit 16 different
-// bank groups.  Operands contiguous along m/n in memory (B of NN, both of TN)
-// are transposed in registers on their way into LDS; the thread mapping of
-// that transpose puts consecutive lanes on consecutive 16-byte k-chunks so the
-// transposed writes are conflict-free too.  Tiles entirely inside the matrix
-// use unconditional 16-byte loads and stores (a block-uniform branch); tiles on
-// the M/N edge and the partial last k-tile use checked element loads.  MFMA
-// 16x16 tiles are issued with the B tile in the instruction's first operand
-// slot, so each lane owns four consecutive columns of one output row.
-// FP16/BF16 use v_mfma_f32_16x16x32_{f16,bf16}; FP32 uses v_mfma_f32_16x16x4_f32.
-// Split-K writes FP32 partials to a workspace and a finishing kernel sums
-// them in split order, then applies the same epilogue.
-#include <algorithm>
-
-#include "common.h"
+// Host side of gemm_bias_act: launch plan (tile size, split-K), argument
+// marshalling into the kernel parameters, and the split-K finishing kernel.
+// The MFMA kernel itself is in gemm_kernel.h, instantiated per operand type
+// in gemm_f16.hip, gemm_bf16.hip and gemm_f32.hip.
+#include "gemm_kernel.h"
 
 namespace ge {
-
-struct EpiParams {
-  float alpha;
-  const float *bias;
-  int act;
-  float slope;
-  const void *aux;
-  int64_t ld_aux;
-  int aux_type;
-  const void *res;
-  int64_t ld_res;
-  int res_type;
-  void *C;
-  int64_t ldc;
-  int c_type;
-  void *pre;
-  int64_t ld_pre;
-  int pre_type;
-  int M, N;
-  int aux_vec, res_vec, c_vec, pre_vec, bias_vec;
-};
-
-struct GemmParams {
-  const void *A;
-  const void *B;
-  int64_t lda, ldb;
-  int M, N, K;
-  int a_vec, b_vec;
-  int tiles_m, tiles_n;
-  int ktiles_per_split;
-  int splits;
-  float *partial;  // [splits][M][N] when splits > 1
-  EpiParams ep;
-};
-
-// Epilogue for four consecutive columns n..n+3 of row m, in three steps so a
-// caller can batch the memory accesses of several rows: the bias of the
-// column group (loaded once per thread), the per-element inputs (aux for the
-// derivative epilogues, residual), then the arithmetic and the store.
-// `fast`: the four columns are inside the matrix and every access is aligned.
-__device__ __forceinline__ void epi_bias(const EpiParams &e, int n, bool fast, float b[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = 0.f;
-  if (!e.bias || n >= e.N) return;
-  if ((fast || n + 3 < e.N) && e.bias_vec) {
-    const f32x4 x = *(const f32x4 *)(e.bias + n);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = x[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = (n + j < e.N) ? e.bias[n + j] : 0.f;
-  }
-}
-
-__device__ __forceinline__ void epi_fetch(const EpiParams &e, int m, int n, bool fast, float a[4], float r[4]) {
-  if (!fast && (m >= e.M || n >= e.N)) return;
-  const bool full = fast || (n + 3) < e.N;
-  if (e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD) {
-    if (full) {
-      load4_any(e.aux, (int64_t)m * e.ld_aux + n, e.aux_type, e.aux_vec, a);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        a[j] = (n + j < e.N) ? load_any(e.aux, (int64_t)m * e.ld_aux + n + j, e.aux_type) : 0.f;
-    }
-  }
-  if (e.res) {
-    if (full) {
-      load4_any(e.res, (int64_t)m * e.ld_res + n, e.res_type, e.res_vec, r);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        r[j] = (n + j < e.N) ? load_any(e.res, (int64_t)m * e.ld_res + n + j, e.res_type) : 0.f;
-    }
-  }
-}
-
-__device__ __forceinline__ void epi_apply(const EpiParams &e, int m, int n, f32x4 acc, const float b[4],
-                                          const float a[4], const float r[4], bool fast) {
-  if (!fast && (m >= e.M || n >= e.N)) return;
-  const bool full = fast || (n + 3) < e.N;
-  float v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = e.alpha * acc[j] + b[j];
-  if (e.pre) {
-    if (full) {
-      store4_any(e.pre, (int64_t)m * e.ld_pre + n, e.pre_type, e.pre_vec, v);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < e.N) store_any(e.pre, (int64_t)m * e.ld_pre + n + j, e.pre_type, v[j]);
-    }
-  }
-  if (e.act == GE_ACT_RELU) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = fmaxf(v[j], 0.f);
-  } else if (e.act == GE_ACT_LRELU_SQ) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float t = v[j] > 0.f ? v[j] : e.slope * v[j];
-      v[j] = t * t;
-    }
-  } else if (e.act == GE_ACT_RELU_MASK_BWD) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = a[j] > 0.f ? v[j] : 0.f;
-  } else if (e.act == GE_ACT_LRELU_SQ_BWD) {
-    const float s2 = 2.f * e.slope * e.slope;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] *= (a[j] > 0.f ? 2.f * a[j] : s2 * a[j]);
-  }
-  if (e.res) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] += r[j];
-  }
-  if (full) {
-    store4_any(e.C, (int64_t)m * e.ldc + n, e.c_type, e.c_vec, v);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (n + j < e.N) store_any(e.C, (int64_t)m * e.ldc + n + j, e.c_type, v[j]);
-  }
-}
-
-// ---- MFMA wrappers: acc += hwA * hwB over one 16-byte-per-lane k chunk -----
-template <typename T> struct Frag;
-template <> struct Frag<half_t> {
-  typedef f16x8 V;
-  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Frag<bf16_t> {
-  typedef bf16x8 V;
-  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Frag<float> {
-  typedef f32x4 V;
-  // four k-steps of 16x16x4: step e pairs element e of both operands, so both
-  // operands see the same k assignment and the sum over the chunk is complete.
-  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
-    return c;
-  }
-};
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// element e of a 16-byte vector holding T values, as raw bits
-template <typename T> __device__ __forceinline__ uint32_t elem_bits(const u32x4 &v, int e) {
-  if constexpr (sizeof(T) == 4) return v[e];
-  else return (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
-}
-template <typename T> __device__ __forceinline__ uint32_t bits_of(T x) {
-  if constexpr (sizeof(T) == 4) return __builtin_bit_cast(uint32_t, x);
-  else return (uint32_t)__builtin_bit_cast(uint16_t, x);
-}
-
-// ---- LDS tile layout ---------------------------------------------------------
-// Tile rows are 128 bytes (eight 16-byte chunks) with no padding; chunk q of
-// row r is stored at chunk q ^ ((r >> 1) & 7).  Measured on gfx950, the MFMA
-// fragment read (16 consecutive rows, one chunk) then runs conflict-free,
-// where a 16-byte row pad costs two-way bank conflicts.
-__device__ __forceinline__ int lds_chunk(int row, int q) { return q ^ ((row >> 1) & 7); }
-
-// ---- tile loaders ------------------------------------------------------------
-// k-contiguous source: R rows (m or n) x BK, each row contiguous along k.
-// Thread t moves vectors v = t + i*NT: row v / VPR, 16-byte chunk v % VPR.
-template <typename T, int R, int BK, int NT> struct LoaderKC {
-  static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int VPR = BK / VEC;  // vectors per row
-  static constexpr int NV = R * VPR / NT;
-  static_assert(NV >= 1 && (R * VPR) % NT == 0, "tile / thread mismatch");
-  u32x4 r[NV];
-
-  __device__ __forceinline__ void load_fast(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * NT;
-      r[i] = *(const u32x4 *)(p + (int64_t)(r0 + v / VPR) * ld + k0 + (v % VPR) * VEC);
-    }
-  }
-  __device__ __forceinline__ void load_checked(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
-                                               int kmax, bool vec, int tid) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * NT;
-      const int gr = r0 + v / VPR, gk = k0 + (v % VPR) * VEC;
-      if (vec && gr < rmax && gk + VEC <= kmax) {
-        r[i] = *(const u32x4 *)(p + (int64_t)gr * ld + gk);
-      } else {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const uint32_t b = (gr < rmax && gk + e < kmax) ? bits_of<T>(p[(int64_t)gr * ld + gk + e]) : 0u;
-          if constexpr (sizeof(T) == 4) w[e] = b;
-          else w[e >> 1] |= b << (16 * (e & 1));
-        }
-        r[i] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(T *s, int stride, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * NT;
-      const int row = v / VPR;
-      *(u32x4 *)(s + row * stride + lds_chunk(row, v % VPR) * VEC) = r[i];
-    }
-  }
-};
-
-// m/n-contiguous source: BK k-rows, each contiguous along the R dimension.
-// Thread t owns k-group kg = t % NKG (KB consecutive k-rows) and vector
-// rv = t / NKG (VEC consecutive rows of the tile); it writes VEC LDS rows of
-// KB k-values.  Consecutive lanes take consecutive k-groups, so one LDS write
-// instruction spreads over distinct 16-byte bank groups.
-template <typename T, int R, int BK, int NT> struct LoaderMC {
-  static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int RV = R / VEC;  // vectors per k-row
-  static constexpr int KB = BK * RV / NT;
-  static constexpr int NKG = BK / KB;
-  static constexpr int W = KB * sizeof(T) / 4;  // dwords per transposed row piece
-  static_assert(KB >= 2 && (BK * RV) % NT == 0 && BK % KB == 0, "tile / thread mismatch");
-  static_assert(W == 1 || W == 2 || W % 4 == 0, "transposed piece must be 4, 8 or 16n bytes");
-  u32x4 x[KB];
-
-  __device__ __forceinline__ void load_fast(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid) {
-    const int kg = tid % NKG, rv = tid / NKG;
-    const T *base = p + (int64_t)(k0 + kg * KB) * ld + r0 + rv * VEC;
-#pragma unroll
-    for (int j = 0; j < KB; ++j) x[j] = *(const u32x4 *)(base + (int64_t)j * ld);
-  }
-  __device__ __forceinline__ void load_checked(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
-                                               int kmax, bool vec, int tid) {
-    const int kg = tid % NKG, rv = tid / NKG;
-    const int gr = r0 + rv * VEC;
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int gk = k0 + kg * KB + j;
-      if (vec && gk < kmax && gr + VEC <= rmax) {
-        x[j] = *(const u32x4 *)(p + (int64_t)gk * ld + gr);
-      } else {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const uint32_t b = (gk < kmax && gr + e < rmax) ? bits_of<T>(p[(int64_t)gk * ld + gr + e]) : 0u;
-          if constexpr (sizeof(T) == 4) w[e] = b;
-          else w[e >> 1] |= b << (16 * (e & 1));
-        }
-        x[j] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(T *s, int stride, int tid) const {
-    const int kg = tid % NKG, rv = tid / NKG;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      // column e of the KB x VEC block: KB k-values of tile row rv*VEC + e
-      uint32_t w[W];
-#pragma unroll
-      for (int q = 0; q < W; ++q) {
-        if constexpr (sizeof(T) == 4) w[q] = elem_bits<T>(x[q], e);
-        else w[q] = elem_bits<T>(x[2 * q], e) | (elem_bits<T>(x[2 * q + 1], e) << 16);
-      }
-      // bytes [b, b + 4W) of tile row `row`; pieces of at most 16 bytes never
-      // straddle a 16-byte chunk, so each is placed by its chunk's swizzle
-      const int row = rv * VEC + e;
-      const int b = kg * KB * (int)sizeof(T);
-      char *rbase = (char *)(s + row * stride);
-      if constexpr (W == 1) {
-        *(uint32_t *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = w[0];
-      } else if constexpr (W == 2) {
-        *(u32x2 *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = u32x2{w[0], w[1]};
-      } else {
-#pragma unroll
-        for (int q = 0; q < W; q += 4)
-          *(u32x4 *)(rbase + lds_chunk(row, (b >> 4) + q / 4) * 16) = u32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
-      }
-    }
-  }
-};
-
-template <typename T, bool KC, int R, int BK, int NT> struct Loader;
-template <typename T, int R, int BK, int NT> struct Loader<T, true, R, BK, NT> : LoaderKC<T, R, BK, NT> {};
-template <typename T, int R, int BK, int NT> struct Loader<T, false, R, BK, NT> : LoaderMC<T, R, BK, NT> {};
-
-// ---- the kernel ---------------------------------------------------------------
-template <typename T, int LAYOUT, int BM, int BN, int BK, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm_kernel(GemmParams p) {
-  constexpr int NT = 64 * WGM * WGN;
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int KCH = 4 * VEC;  // k covered by one 16-byte-per-lane fragment
-  constexpr int STRIDE = BK;  // 128-byte rows, 16-byte chunks XOR-swizzled by row
-  static_assert(BK * sizeof(T) == 128, "the LDS swizzle assumes 128-byte tile rows");
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr bool A_KC = (LAYOUT != GE_TN);
-  constexpr bool B_KC = (LAYOUT == GE_NT);
-  constexpr bool PING_PONG = (WGM == 2 && WGN * WGM == 8);
-  static_assert(BK % KCH == 0, "BK must hold whole fragments");
-  typedef typename Frag<T>::V V;
-
-  // operand tiles (double-buffered); after the k loop the same memory stages
-  // the FP32 accumulator tile for the epilogue
-  constexpr int OPER_BYTES = 2 * (BM + BN) * STRIDE * (int)sizeof(T);
-  constexpr int NPASS = BM >= 256 ? 2 : 1;  // row passes of the staged epilogue
-  constexpr int RP = BM / NPASS;
-  constexpr int CSTRIDE = BN + 4;  // floats per staged row (16-byte pad)
-  constexpr int STAGE_BYTES = RP * CSTRIDE * 4;
-  constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
-  static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
-  static_assert(BM / WGM <= RP && RP % (BM / WGM) == 0, "a wave's rows must fall in one pass");
-  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
-  T(*sA)[BM * STRIDE] = (T(*)[BM * STRIDE])smem;
-  T(*sB)[BN * STRIDE] = (T(*)[BN * STRIDE])(smem + 2 * BM * STRIDE * sizeof(T));
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave / WGN) * WTM, wn0 = (wave % WGN) * WTN;
-
-  // block -> tile: spread consecutive tiles over one XCD, then group along M
-  int bid = blockIdx.x;
-  const int total = p.tiles_m * p.tiles_n;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  constexpr int GROUP = 8;
-  const int per_group = GROUP * p.tiles_n;
-  const int first_m = (bid / per_group) * GROUP;
-  const int gsize = min(p.tiles_m - first_m, GROUP);
-  const int tm = first_m + (bid % per_group) % gsize;
-  const int tn = (bid % per_group) / gsize;
-  const int bm0 = tm * BM, bn0 = tn * BN;
-
-  const int nk_total = (p.K + BK - 1) / BK;
-  const int nk_full = p.K / BK;
-  const int kt0 = blockIdx.z * p.ktiles_per_split;
-  const int kt1 = min(nk_total, kt0 + p.ktiles_per_split);
-  const bool interior = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && p.a_vec && p.b_vec;
-
-  const T *__restrict__ Ap = (const T *)p.A;
-  const T *__restrict__ Bp = (const T *)p.B;
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // lane reads tile row (block + lane % 16) at 16-byte chunk 4c + lane / 16;
-  // rows of a fragment start at multiples of 16, so the swizzle depends on
-  // the lane only
-  constexpr int NCH = BK / KCH;
-  const int arow = (wm0 + (lane & 15)) * STRIDE;
-  const int brow = (wn0 + (lane & 15)) * STRIDE;
-  int koff[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) koff[c] = lds_chunk(lane & 15, 4 * c + (lane >> 4)) * VEC;
-
-  // MFMAs over one LDS buffer.  Software-pipelined fragment reads: the k-tile
-  // is a sequence of S = NC*FM A fragments (chunk c, row block i); the read of
-  // fragment s+2 is issued before the MFMAs of fragment s, and the B fragments
-  // of chunk c+1 halfway through chunk c, so each LDS read has MFMA work in
-  // flight to hide its latency.  Scheduling barriers keep that order.
-  auto compute = [&](int buf) {
-    const T *a_s = sA[buf] + arow;
-    const T *b_s = sB[buf] + brow;
-    constexpr int NC = BK / KCH;
-    constexpr int S = NC * FM;
-    V af[S], bf[NC][FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) bf[0][j] = *(const V *)(b_s + j * 16 * STRIDE + koff[0]);
-#pragma unroll
-    for (int s = 0; s < 2 && s < S; ++s)
-      af[s] = *(const V *)(a_s + (s % FM) * 16 * STRIDE + koff[s / FM]);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int c = s / FM, i = s % FM;
-      if (s + 2 < S) af[s + 2] = *(const V *)(a_s + ((s + 2) % FM) * 16 * STRIDE + koff[(s + 2) / FM]);
-      if (i == FM / 2 && c + 1 < NC) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bf[c + 1][j] = *(const V *)(b_s + j * 16 * STRIDE + koff[c + 1]);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = Frag<T>::mma(bf[c][j], af[s], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  if constexpr (PING_PONG) {
-    // Two wave groups (rows 0..BM/2 and BM/2..BM of the tile; one wave of
-    // each group per SIMD) alternate: while one group multiplies tile k the
-    // other stores its half of tile k+1 (loaded one iteration earlier) into
-    // the other LDS buffer and issues the global loads of its half of tile
-    // k+2.  So every SIMD always has one wave issuing MFMAs, and each global
-    // load has a whole iteration to arrive.
-    const int g = wave / WGN;
-    const int gt = tid % (NT / 2);
-    Loader<T, A_KC, BM / 2, BK, NT / 2> la;
-    Loader<T, B_KC, BN / 2, BK, NT / 2> lb;
-    const int ar0 = bm0 + g * (BM / 2), br0 = bn0 + g * (BN / 2);
-    auto load_half = [&](int kt) {
-      if (interior && kt < nk_full) {
-        la.load_fast(Ap, p.lda, ar0, kt * BK, gt);
-        lb.load_fast(Bp, p.ldb, br0, kt * BK, gt);
-      } else {
-        la.load_checked(Ap, p.lda, ar0, p.M, kt * BK, p.K, p.a_vec, gt);
-        lb.load_checked(Bp, p.ldb, br0, p.N, kt * BK, p.K, p.b_vec, gt);
-      }
-    };
-    auto store_half = [&](int buf) {
-      la.store(sA[buf] + g * (BM / 2) * STRIDE, STRIDE, gt);
-      lb.store(sB[buf] + g * (BN / 2) * STRIDE, STRIDE, gt);
-    };
-    auto memory_phase = [&](int kt, int buf) {
-      if (kt + 1 < kt1) {
-        store_half(buf ^ 1);
-        if (kt + 2 < kt1) load_half(kt + 2);
-      }
-    };
-    if (kt0 < kt1) {
-      load_half(kt0);
-      store_half(0);
-      if (kt0 + 1 < kt1) load_half(kt0 + 1);
-      __syncthreads();
-    }
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int buf = (kt - kt0) & 1;
-      if (g == 0) {
-        __builtin_amdgcn_s_setprio(1);
-        compute(buf);
-        __builtin_amdgcn_s_setprio(0);
-      } else {
-        memory_phase(kt, buf);
-      }
-      __syncthreads();
-      if (g == 1) {
-        __builtin_amdgcn_s_setprio(1);
-        compute(buf);
-        __builtin_amdgcn_s_setprio(0);
-      } else {
-        memory_phase(kt, buf);
-      }
-      __syncthreads();
-    }
-  } else {
-    Loader<T, A_KC, BM, BK, NT> la;
-    Loader<T, B_KC, BN, BK, NT> lb;
-    auto load_tile = [&](int kt) {
-      if (interior && kt < nk_full) {
-        la.load_fast(Ap, p.lda, bm0, kt * BK, tid);
-        lb.load_fast(Bp, p.ldb, bn0, kt * BK, tid);
-      } else {
-        la.load_checked(Ap, p.lda, bm0, p.M, kt * BK, p.K, p.a_vec, tid);
-        lb.load_checked(Bp, p.ldb, bn0, p.N, kt * BK, p.K, p.b_vec, tid);
-      }
-    };
-    if (kt0 < kt1) {
-      load_tile(kt0);
-      la.store(sA[0], STRIDE, tid);
-      lb.store(sB[0], STRIDE, tid);
-      __syncthreads();
-    }
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int cur = (kt - kt0) & 1;
-      const bool more = kt + 1 < kt1;
-      if (more) load_tile(kt + 1);
-      compute(cur);
-      if (more) {
-        la.store(sA[cur ^ 1], STRIDE, tid);
-        lb.store(sB[cur ^ 1], STRIDE, tid);
-      }
-      __syncthreads();
-    }
-  }
-
-  // Epilogue: the lane owning C[m][n..n+3] of each 16x16 fragment writes it
-  // to the staged tile in LDS; then all threads walk the staged rows, four
-  // consecutive columns per thread, so global stores are whole-row coalesced.
-  const EpiParams &e = p.ep;
-  const bool fast = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && e.c_vec && (!e.aux || e.aux_vec) &&
-                    (!e.res || e.res_vec) && (!e.pre || e.pre_vec) && (!e.bias || e.bias_vec);
-  float *cs = (float *)smem;
-  float *part = p.splits > 1 ? p.partial + (int64_t)blockIdx.z * p.M * p.N : nullptr;
-  const bool pvec = (p.N & 3) == 0;
-  // each thread owns one group of four columns and rows r0, r0 + RS, ...
-  constexpr int CG = BN / 4;
-  static_assert(NT % CG == 0, "threads must tile whole staged rows");
-  constexpr int RS = NT / CG;
-  constexpr int RPT = RP / RS;
-  // rows whose loads are issued together (fewer while a second pass still
-  // holds its accumulators in registers)
-  constexpr int EU = NPASS > 1 ? 2 : (RPT >= 4 ? 4 : RPT);
-  static_assert(RPT % EU == 0, "rows per thread must split into batches");
-  const int cg = tid % CG, r0 = tid / CG;
-  const int n = bn0 + cg * 4;
-  float bias[4];
-  epi_bias(e, n, fast, bias);
-  for (int pass = 0; pass < NPASS; ++pass) {
-    if (wm0 / RP == pass) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wm0 - pass * RP + i * 16 + (lane & 15);
-          const int col = wn0 + j * 16 + (lane >> 4) * 4;
-          *(f32x4 *)(cs + row * CSTRIDE + col) = acc[i][j];
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q0 = 0; q0 < RPT; q0 += EU) {
-      f32x4 v[EU];
-      float a[EU][4], r[EU][4];
-#pragma unroll
-      for (int u = 0; u < EU; ++u) {
-        const int rr = r0 + (q0 + u) * RS;
-        v[u] = *(const f32x4 *)(cs + rr * CSTRIDE + cg * 4);
-        if (part == nullptr) epi_fetch(e, bm0 + pass * RP + rr, n, fast, a[u], r[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < EU; ++u) {
-        const int m = bm0 + pass * RP + r0 + (q0 + u) * RS;
-        if (part == nullptr) {
-          epi_apply(e, m, n, v[u], bias, a[u], r[u], fast);
-        } else if (m < p.M && n < p.N) {
-          float *dst = part + (int64_t)m * p.N + n;
-          if (pvec && n + 3 < p.N) {
-            *(f32x4 *)dst = v[u];
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (n + q < p.N) dst[q] = v[u][q];
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
 
 // Sums split-K partials in split order and applies the epilogue.
 __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p) {
@@ -604,34 +35,47 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p) {
 // ---- host launcher --------------------------------------------------------------
 namespace {
 
-struct Plan {
-  int tile;  // 256, 128 or 64 (square tiles)
-  int BK;
-  int tiles_m, tiles_n, nk, splits, kps;
-};
-
 int64_t ntiles(int64_t M, int64_t N, int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); }
 
 Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   Plan pl;
   const int bk = ab_type == GE_F32 ? 32 : 64;
-  // the largest square tile that still gives most of the 256 CUs a tile
-  if (ntiles(M, N, 256) >= 192) pl.tile = 256;
-  else if (ntiles(M, N, 128) >= 160) pl.tile = 128;
-  else pl.tile = 64;
+  const int nk = (int)((K + bk - 1) / bk);
+  const int64_t t256 = ntiles(M, N, 256);
+  int s = 0;  // 0: chosen below with the tile
+  // The 256x256 tile is the most efficient per k-step.  Use it when the
+  // output alone gives most of the 256 CUs a tile, or when K is long enough
+  // that splitting it (at least 8 k-tiles per split) fills the CUs: measured
+  // on weight-gradient shapes (K = batch 4096), the split-K partial traffic
+  // costs less than running smaller, slower tiles.
+  if (N <= 16 && M > 16) {
+    // one narrow column of tiles; split-K supplies the parallelism
+    pl.bm = 128;
+    pl.bn = 16;
+  } else if (t256 >= 192) {
+    pl.bm = pl.bn = 256;
+  } else if (split_k < 1 && nk >= 48 && t256 * std::min<int64_t>(nk / 8, 64) >= 192) {
+    pl.bm = pl.bn = 256;
+    s = (int)std::min<int64_t>({(256 + t256 - 1) / t256, nk / 8, 64});
+  } else if (ntiles(M, N, 128) >= 160) {
+    pl.bm = pl.bn = 128;
+  } else {
+    pl.bm = pl.bn = 64;
+  }
   pl.BK = bk;
-  pl.tiles_m = (int)((M + pl.tile - 1) / pl.tile);
-  pl.tiles_n = (int)((N + pl.tile - 1) / pl.tile);
-  pl.nk = (int)((K + bk - 1) / bk);
-  int s = 1;
+  pl.tiles_m = (int)((M + pl.bm - 1) / pl.bm);
+  pl.tiles_n = (int)((N + pl.bn - 1) / pl.bn);
+  pl.nk = nk;
   if (split_k >= 1) {
     s = split_k;
-  } else {
+  } else if (s == 0) {
+    s = 1;
     const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
     // split long K loops when the output alone cannot fill the 256 CUs
     if (tiles < 256 && pl.nk >= 16) {
-      int64_t want = (512 + tiles - 1) / tiles;
-      s = (int)std::min<int64_t>(want, pl.nk / 8);
+      // (a narrow tile is bound by reading A, so short splits still pay)
+      const int64_t want = (512 + tiles - 1) / tiles;
+      s = (int)std::min<int64_t>(want, pl.nk / (pl.bn == 16 ? 2 : 8));
       s = std::max(1, std::min(s, 64));
     }
   }
@@ -639,25 +83,6 @@ Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   pl.kps = (pl.nk + s - 1) / s;
   pl.splits = pl.kps > 0 ? (pl.nk + pl.kps - 1) / pl.kps : 1;
   return pl;
-}
-
-template <typename T, int LAYOUT>
-void launch_t(const Plan &pl, const GemmParams &gp, hipStream_t s) {
-  dim3 grid(pl.tiles_m * pl.tiles_n, 1, pl.splits);
-  constexpr int BK = sizeof(T) == 4 ? 32 : 64;
-  if (pl.tile == 256)
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 256, 256, BK, 2, 4>), grid, dim3(512), 0, s, gp);
-  else if (pl.tile == 128)
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 128, 128, BK, 2, 2>), grid, dim3(256), 0, s, gp);
-  else
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 64, 64, BK, 2, 2>), grid, dim3(256), 0, s, gp);
-}
-
-template <typename T>
-void launch_layout(int layout, const Plan &pl, const GemmParams &gp, hipStream_t s) {
-  if (layout == GE_NN) launch_t<T, GE_NN>(pl, gp, s);
-  else if (layout == GE_NT) launch_t<T, GE_NT>(pl, gp, s);
-  else launch_t<T, GE_TN>(pl, gp, s);
 }
 
 }  // namespace
@@ -726,9 +151,9 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
   e.pre_vec = al4(a.pre, a.ld_pre, a.pre_type);
   e.bias_vec = a.bias ? (((uintptr_t)a.bias % 16) == 0) : 0;
 
-  if (a.ab_type == GE_F16) launch_layout<half_t>(a.layout, pl, gp, s);
-  else if (a.ab_type == GE_BF16) launch_layout<bf16_t>(a.layout, pl, gp, s);
-  else launch_layout<float>(a.layout, pl, gp, s);
+  if (a.ab_type == GE_F16) gemm_dispatch_f16(a.layout, pl, gp, s);
+  else if (a.ab_type == GE_BF16) gemm_dispatch_bf16(a.layout, pl, gp, s);
+  else gemm_dispatch_f32(a.layout, pl, gp, s);
   int st = launch_status("gemm_bias_act");
   if (st != GE_OK || pl.splits <= 1) return st;
   const int64_t items = a.M * ((a.N + 3) / 4);

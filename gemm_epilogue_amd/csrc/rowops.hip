@@ -18,44 +18,81 @@ namespace ge {
 // "Capstone 5: train a network with your CUDA kernels", section "Work through
 // the backward pass": db = sum_rows(dZ), a reduction across the batch.
 //
-// A block of 256 threads owns 256 consecutive columns (four per lane) and a
-// contiguous range of rows; wave w sums rows w, w+4, w+8, ... of the range in
-// order, then the four wave partials are added in wave order.  With several
-// row ranges the partials go to a workspace and colsum_final adds them in
-// range order.
-constexpr int CS_COLS = 256;
-constexpr int CS_ROWS_MIN = 64;
+// A block of 256 threads owns 512 consecutive columns (eight per lane, one
+// 16-byte load for 16-bit data) and a contiguous range of rows; wave w sums
+// rows w, w+4, w+8, ... of the range in row order, keeping four rows' loads
+// in flight, then the four wave partials are added in wave order.  With
+// several row ranges the partials go to a workspace and colsum_final adds
+// them: wave w of a final block takes ranges w, w+4, ... in order and the
+// four wave sums are again added in wave order.
+constexpr int CS_VEC = 8;
+constexpr int CS_COLS = 64 * CS_VEC;
+constexpr int CS_ROWS_MIN = 32;
+constexpr int CS_UNROLL = 4;
 
-__global__ __launch_bounds__(256) void colsum_partial_kernel(const void *__restrict__ X, int M, int N,
-                                                             int64_t ldx, int xt, int vec, int rows_per,
-                                                             float alpha, float *__restrict__ out) {
-  __shared__ float red[4][CS_COLS];
+template <typename T>
+__device__ __forceinline__ void cs_load8(const T *__restrict__ X, int64_t i, bool full, int left, float v[8]) {
+  if (full) {
+    if constexpr (sizeof(T) == 4) {
+      const f32x4 a = *(const f32x4 *)(X + i), b = *(const f32x4 *)(X + i + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = a[j];
+        v[4 + j] = b[j];
+      }
+    } else {
+      typedef T T8 __attribute__((ext_vector_type(8)));
+      const T8 x = *(const T8 *)(X + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (float)x[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = j < left ? (float)X[i + j] : 0.f;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const T *__restrict__ X, int M, int N, int64_t ldx,
+                                                             int vec, int rows_per, float alpha,
+                                                             float *__restrict__ out) {
+  __shared__ float red[3][CS_COLS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = blockIdx.x * CS_COLS + lane * 4;
+  const int n = blockIdx.x * CS_COLS + lane * CS_VEC;
   const int r0 = blockIdx.y * rows_per;
   const int r1 = min(M, r0 + rows_per);
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (n < N) {
-    const bool full = n + 3 < N;
-    for (int r = r0 + wave; r < r1; r += 4) {
-      float v[4];
-      if (full) {
-        load4_any(X, (int64_t)r * ldx + n, xt, vec, v);
-      } else {
-        for (int j = 0; j < 4; ++j) v[j] = (n + j < N) ? load_any(X, (int64_t)r * ldx + n + j, xt) : 0.f;
-      }
+    const bool full = vec && n + CS_VEC <= N;
+    const int left = N - n;
+    int r = r0 + wave;
+    for (; r + 4 * (CS_UNROLL - 1) < r1; r += 4 * CS_UNROLL) {
+      float v[CS_UNROLL][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] += v[j];
+      for (int u = 0; u < CS_UNROLL; ++u) cs_load8(X, (int64_t)(r + 4 * u) * ldx + n, full, left, v[u]);
+#pragma unroll
+      for (int u = 0; u < CS_UNROLL; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] += v[u][j];
+    }
+    for (; r < r1; r += 4) {
+      float v[8];
+      cs_load8(X, (int64_t)r * ldx + n, full, left, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[j] += v[j];
     }
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) red[wave][lane * 4 + j] = s[j];
+    for (int j = 0; j < 8; ++j) red[wave - 1][lane * CS_VEC + j] = s[j];
+  }
   __syncthreads();
   if (wave == 0 && n < N) {
     float *dst = out + (int64_t)blockIdx.y * N;
-    for (int j = 0; j < 4; ++j) {
-      const int c = lane * 4 + j;
-      const float t = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = lane * CS_VEC + j;
+      const float t = ((s[j] + red[0][c]) + red[1][c]) + red[2][c];
       if (n + j < N) dst[n + j] = alpha * t;
     }
   }
@@ -63,11 +100,24 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const void *__restr
 
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restrict__ part, int splits, int N,
                                                            float alpha, float *__restrict__ out) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float red[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * N + n];
-  out[n] = alpha * s;
+  if (n < N) {
+    int k = wave;
+    for (; k + 4 * 7 < splits; k += 4 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(k + 4 * u) * N + n];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < splits; k += 4) s += part[(int64_t)k * N + n];
+  }
+  if (wave > 0) red[wave - 1][lane] = s;
+  __syncthreads();
+  if (wave == 0 && n < N) out[n] = alpha * (((s + red[0][lane]) + red[1][lane]) + red[2][lane]);
 }
 
 namespace {
@@ -77,6 +127,20 @@ int colsum_splits(int64_t M, int64_t N) {
   int64_t want = (1024 + colblocks - 1) / colblocks;
   int64_t maxs = std::max<int64_t>(1, M / CS_ROWS_MIN);
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(maxs, 1024)));
+}
+
+template <typename T>
+void colsum_partial(dim3 grid, hipStream_t st, const void *X, int M, int N, int64_t ldx, int vec, int rows_per,
+                    float alpha, float *out) {
+  hipLaunchKernelGGL(colsum_partial_kernel<T>, grid, dim3(256), 0, st, (const T *)X, M, N, ldx, vec, rows_per,
+                     alpha, out);
+}
+
+void colsum_partial_any(int xt, dim3 grid, hipStream_t st, const void *X, int M, int N, int64_t ldx, int vec,
+                        int rows_per, float alpha, float *out) {
+  if (xt == GE_F32) colsum_partial<float>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out);
+  else if (xt == GE_F16) colsum_partial<half_t>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out);
+  else colsum_partial<bf16_t>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out);
 }
 }  // namespace
 
@@ -89,12 +153,12 @@ int64_t colsum_ws_bytes(int64_t M, int64_t N) {
 int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt, float alpha, float *out,
                   void *ws, int64_t ws_bytes, hipStream_t st) {
   if (N == 0) return GE_OK;
-  const int vec = vec_aligned(X, ldx, dtype_size(xt), 4 * dtype_size(xt));
+  const int vec = vec_aligned(X, ldx, dtype_size(xt), 16);
   const int colblocks = (int)((N + CS_COLS - 1) / CS_COLS);
   const int splits = M > 0 ? colsum_splits(M, N) : 1;
   if (splits == 1) {
-    hipLaunchKernelGGL(colsum_partial_kernel, dim3(colblocks, 1), dim3(256), 0, st, X, (int)M, (int)N, ldx,
-                       xt, vec, (int)std::max<int64_t>(M, 1), alpha, out);
+    colsum_partial_any(xt, dim3(colblocks, 1), st, X, (int)M, (int)N, ldx, vec, (int)std::max<int64_t>(M, 1),
+                       alpha, out);
     return launch_status("colsum");
   }
   const int64_t need = (int64_t)splits * N * 4;
@@ -103,11 +167,10 @@ int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt, floa
     return GE_E_WORKSPACE;
   }
   const int rows_per = (int)((M + splits - 1) / splits);
-  hipLaunchKernelGGL(colsum_partial_kernel, dim3(colblocks, splits), dim3(256), 0, st, X, (int)M, (int)N,
-                     ldx, xt, vec, rows_per, 1.0f, (float *)ws);
+  colsum_partial_any(xt, dim3(colblocks, splits), st, X, (int)M, (int)N, ldx, vec, rows_per, 1.0f, (float *)ws);
   int s = launch_status("colsum (partial)");
   if (s != GE_OK) return s;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st,
                      (const float *)ws, splits, (int)N, alpha, out);
   return launch_status("colsum (final)");
 }

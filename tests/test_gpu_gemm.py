@@ -38,8 +38,11 @@ def _tol(fmt):
     return TOL_F32 if fmt == "f32" else TOL_LOWP
 
 
+# includes narrow outputs (N <= 16: 128x16 tiles with short K splits) and a
+# long-K shape that takes 256x256 tiles with split-K
 RAGGED = [(1, 1, 1), (15, 17, 63), (65, 130, 100), (200, 72, 784), (130, 257, 129),
-          (1800, 1800, 130), (96, 80, 3000)]
+          (1800, 1800, 130), (96, 80, 3000), (300, 10, 1000), (33, 1, 70), (4096, 16, 2048),
+          (1000, 700, 8200)]
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16", "f32"])
@@ -99,6 +102,25 @@ def test_gemm_epilogue_variants(ge, act, fmt):
                            aux=dev(aux, fmt), residual=dev(res, fmt), pre=pre, out_dtype=TD[fmt])
     assert_parity(host(out), ref, TOL_LOWP, fmt, f"{act} C")
     assert_parity(host(pre), pre_ref, TOL_LOWP, fmt, f"{act} pre")
+
+
+@pytest.mark.parametrize("act", ["relu_mask_bwd", "lrelu_sq_bwd"])
+@pytest.mark.parametrize("fmt,aux_fmt,out_fmt", [("f32", "f32", "f32"), ("f16", "f16", "f16"),
+                                                 ("f16", "f32", "f32"), ("bf16", "bf16", "f32"),
+                                                 ("f16", "f16", "f32")])
+@pytest.mark.parametrize("shape", [(128, 256, 10), (512, 384, 200), (300, 200, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_derivative_epilogue_aux_only(ge, act, fmt, aux_fmt, out_fmt, shape):
+    """Backward epilogues with aux and no residual, on interior (aligned) and edge tiles."""
+    M, N, K = shape
+    sa, sb = shapes_of(M, N, K, "NT")
+    A = datagen.normal(sa, 1.0, seed=M + K, fmt=fmt)
+    B = datagen.normal(sb, 0.05, seed=N + K, fmt=fmt)
+    aux = datagen.normal((M, N), 1.0, seed=M + N, fmt=aux_fmt)
+    ref, _ = oracle.gemm_epilogue(A, B, "NT", 1.0, None, act, 0.5, aux, None, out_fmt=out_fmt)
+    out = ge.gemm_bias_act(dev(A, fmt), dev(B, fmt), "NT", act=act, slope=0.5, aux=dev(aux, aux_fmt),
+                           out_dtype=TD[out_fmt])
+    assert_parity(host(out), ref, _tol(fmt), out_fmt, f"{act} {fmt}/{aux_fmt}/{out_fmt} {shape}")
 
 
 def test_gemm_strided_and_unaligned_operands(ge):
