@@ -109,6 +109,8 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
   gp.K = (int)a.K;
   gp.a_vec = vec_aligned(a.A, a.lda, es, 16);
   gp.b_vec = vec_aligned(a.B, a.ldb, es, 16);
+  // the fast loads address up to 64 operand rows from one per-thread 32-bit offset
+  gp.off32 = (a.lda * es * 64 < ((int64_t)1 << 31)) && (a.ldb * es * 64 < ((int64_t)1 << 31));
   gp.tiles_m = pl.tiles_m;
   gp.tiles_n = pl.tiles_n;
   gp.ktiles_per_split = pl.kps;

@@ -60,6 +60,7 @@ struct GemmParams {
   int64_t lda, ldb;
   int M, N, K;
   int a_vec, b_vec;
+  int off32;  // per-thread operand offsets of the fast loads fit in 31 bits
   int tiles_m, tiles_n;
   int ktiles_per_split;
   int splits;
@@ -286,6 +287,32 @@ template <> struct Frag<float> {
   }
 };
 
+// The same products with the accumulator pinned to the accumulation
+// registers (AGPRs), for the kernel whose 256 accumulator registers per lane
+// fill that file: with the builtin the register allocator moves accumulators
+// between the two register files inside the k loop.
+template <typename T> struct FragA;
+template <> struct FragA<half_t> {
+  static __device__ __forceinline__ void mma(const f16x8 &a, const f16x8 &b, f32x4 &c) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+};
+template <> struct FragA<bf16_t> {
+  static __device__ __forceinline__ void mma(const bf16x8 &a, const bf16x8 &b, f32x4 &c) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+};
+template <> struct FragA<float> {
+  static __device__ __forceinline__ void mma(const f32x4 &a, const f32x4 &b, f32x4 &c) {
+    asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0\n\t"
+                 "v_mfma_f32_16x16x4_f32 %0, %3, %4, %0\n\t"
+                 "v_mfma_f32_16x16x4_f32 %0, %5, %6, %0\n\t"
+                 "v_mfma_f32_16x16x4_f32 %0, %7, %8, %0"
+                 : "+a"(c)
+                 : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]));
+  }
+};
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -301,10 +328,16 @@ template <typename T> __device__ __forceinline__ uint32_t bits_of(T x) {
 
 // ---- LDS tile layout ---------------------------------------------------------
 // Tile rows are 128 bytes (eight 16-byte chunks) with no padding; chunk q of
-// row r is stored at chunk q ^ ((r >> 1) & 7).  Measured on gfx950, the MFMA
-// fragment read (16 consecutive rows, one chunk) then runs conflict-free,
-// where a 16-byte row pad costs two-way bank conflicts.
-__device__ __forceinline__ int lds_chunk(int row, int q) { return q ^ ((row >> 1) & 7); }
+// row r is stored at chunk q ^ s(r >> 1), s(p) = 4 (p & 1) + ((p >> 1) & 3).
+// s takes all eight values over eight consecutive row pairs, so the MFMA
+// fragment read (16 consecutive rows, one chunk) hits 16 distinct bank
+// groups; consecutive row pairs differ in bit 2 of s, so a write of half a
+// row (one 32-wide k-chunk) by 16 lanes covering four rows does as well.
+// (A 16-byte row pad costs two-way conflicts on the fragment reads.)
+__device__ __forceinline__ int lds_chunk(int row, int q) {
+  const int p = row >> 1;
+  return q ^ (((p & 1) << 2) | ((p >> 1) & 3));
+}
 
 // ---- tile loaders ------------------------------------------------------------
 // k-contiguous source: R rows (m or n) x BK, each row contiguous along k.
@@ -319,12 +352,51 @@ template <typename T, int R, int BK, int NT> struct LoaderKC {
   static_assert(PART || NVEC % NT == 0, "tile / thread mismatch");
   u32x4 r[NV];
 
+  // vector i of thread t sits at tile row t / VPR + i * (NT / VPR): a
+  // block-uniform row base plus one 32-bit per-thread byte offset (the host
+  // only takes this path when NT / VPR rows of the operand span < 2 GiB)
   __device__ __forceinline__ void load_fast(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid) {
+    if constexpr (PART) {
+      if (tid < NVEC) r[0] = *(const u32x4 *)(p + (int64_t)(r0 + tid / VPR) * ld + k0 + (tid % VPR) * VEC);
+    } else {
+      static_assert(NT % VPR == 0, "whole rows per round");
+      const uint32_t off = (uint32_t)(((tid / VPR) * ld + (tid % VPR) * VEC) * (int64_t)sizeof(T));
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
+      for (int i = 0; i < NV; ++i) {
+        const char *base = (const char *)(p + (int64_t)(r0 + i * (NT / VPR)) * ld + k0);
+        r[i] = *(const u32x4 *)(base + off);
+      }
+    }
+  }
+  // single fast loads / LDS writes, for spreading them over MFMA work
+  static constexpr int NLOAD = NV, NSTORE = NV;
+  __device__ __forceinline__ void load_piece(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid, int i) {
+    const uint32_t off = (uint32_t)(((tid / VPR) * ld + (tid % VPR) * VEC) * (int64_t)sizeof(T));
+    const char *base = (const char *)(p + (int64_t)(r0 + i * (NT / VPR)) * ld + k0);
+    r[i] = *(const u32x4 *)(base + off);
+  }
+  // qoff: 16-byte chunk offset of this k-slice within the LDS row
+  __device__ __forceinline__ void store_piece(T *s, int stride, int tid, int i, int qoff = 0) const {
+    const int v = tid + i * NT;
+    const int row = v / VPR;
+    *(u32x4 *)(s + row * stride + lds_chunk(row, v % VPR + qoff) * VEC) = r[i];
+  }
+  // quarters of the same
+  __device__ __forceinline__ void load_fast_q(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid, int q) {
+    static_assert(!PART && NV % 4 == 0, "quarters of whole rounds");
+    const uint32_t off = (uint32_t)(((tid / VPR) * ld + (tid % VPR) * VEC) * (int64_t)sizeof(T));
+#pragma unroll
+    for (int i = q * NV / 4; i < (q + 1) * NV / 4; ++i) {
+      const char *base = (const char *)(p + (int64_t)(r0 + i * (NT / VPR)) * ld + k0);
+      r[i] = *(const u32x4 *)(base + off);
+    }
+  }
+  __device__ __forceinline__ void store_q(T *s, int stride, int tid, int q) const {
+#pragma unroll
+    for (int i = q * NV / 4; i < (q + 1) * NV / 4; ++i) {
       const int v = tid + i * NT;
-      if (PART && v >= NVEC) continue;
-      r[i] = *(const u32x4 *)(p + (int64_t)(r0 + v / VPR) * ld + k0 + (v % VPR) * VEC);
+      const int row = v / VPR;
+      *(u32x4 *)(s + row * stride + lds_chunk(row, v % VPR) * VEC) = r[i];
     }
   }
   __device__ __forceinline__ void load_checked(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
@@ -378,12 +450,17 @@ template <typename T, int R, int BK, int NT> struct LoaderMC {
   static_assert(W == 1 || W == 2 || W % 4 == 0, "transposed piece must be 4, 8 or 16n bytes");
   u32x4 x[KB];
 
+  // k-row j of thread t: a block-uniform row base plus one 32-bit per-thread
+  // byte offset
   __device__ __forceinline__ void load_fast(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid) {
     if (PART && tid >= ACTIVE) return;
     const int kg = tid % NKG, rv = tid / NKG;
-    const T *base = p + (int64_t)(k0 + kg * KB) * ld + r0 + rv * VEC;
+    const uint32_t off = (uint32_t)(((int64_t)(kg * KB) * ld + rv * VEC) * (int64_t)sizeof(T));
 #pragma unroll
-    for (int j = 0; j < KB; ++j) x[j] = *(const u32x4 *)(base + (int64_t)j * ld);
+    for (int j = 0; j < KB; ++j) {
+      const char *base = (const char *)(p + (int64_t)(k0 + j) * ld + r0);
+      x[j] = *(const u32x4 *)(base + off);
+    }
   }
   __device__ __forceinline__ void load_checked(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
                                                int kmax, bool vec, int tid) {
@@ -407,39 +484,184 @@ template <typename T, int R, int BK, int NT> struct LoaderMC {
       }
     }
   }
+  // transposed write of column e of the KB x VEC block: KB k-values of tile
+  // row rv*VEC + e
+  __device__ __forceinline__ void store_e(T *s, int stride, int kg, int rv, int e, int qoff = 0) const {
+    uint32_t w[W];
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      if constexpr (sizeof(T) == 4) w[q] = elem_bits<T>(x[q], e);
+      else w[q] = elem_bits<T>(x[2 * q], e) | (elem_bits<T>(x[2 * q + 1], e) << 16);
+    }
+    // bytes [b, b + 4W) of tile row `row`; pieces of at most 16 bytes never
+    // straddle a 16-byte chunk, so each is placed by its chunk's swizzle
+    const int row = rv * VEC + e;
+    const int b = kg * KB * (int)sizeof(T) + qoff * 16;
+    char *rbase = (char *)(s + row * stride);
+    if constexpr (W == 1) {
+      *(uint32_t *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = w[0];
+    } else if constexpr (W == 2) {
+      *(u32x2 *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = u32x2{w[0], w[1]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < W; q += 4)
+        *(u32x4 *)(rbase + lds_chunk(row, (b >> 4) + q / 4) * 16) = u32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
+    }
+  }
   __device__ __forceinline__ void store(T *s, int stride, int tid) const {
     if (PART && tid >= ACTIVE) return;
     const int kg = tid % NKG, rv = tid / NKG;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      // column e of the KB x VEC block: KB k-values of tile row rv*VEC + e
-      uint32_t w[W];
+    for (int e = 0; e < VEC; ++e) store_e(s, stride, kg, rv, e);
+  }
+  // single fast loads (k-row j) and transposed LDS writes (column e); every
+  // write reads all KB loaded vectors, so a step's writes precede its loads
+  static constexpr int NLOAD = KB, NSTORE = VEC;
+  __device__ __forceinline__ void load_piece(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid, int j) {
+    const int kg = tid % NKG, rv = tid / NKG;
+    const uint32_t off = (uint32_t)(((int64_t)(kg * KB) * ld + rv * VEC) * (int64_t)sizeof(T));
+    const char *base = (const char *)(p + (int64_t)(k0 + j) * ld + r0);
+    x[j] = *(const u32x4 *)(base + off);
+  }
+  __device__ __forceinline__ void store_piece(T *s, int stride, int tid, int e, int qoff = 0) const {
+    store_e(s, stride, tid % NKG, tid / NKG, e, qoff);
+  }
+  // quarters of the fast loads and of the LDS writes
+  __device__ __forceinline__ void load_fast_q(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid, int q) {
+    static_assert(!PART && KB % 4 == 0, "quarters of whole rounds");
+    const int kg = tid % NKG, rv = tid / NKG;
+    const uint32_t off = (uint32_t)(((int64_t)(kg * KB) * ld + rv * VEC) * (int64_t)sizeof(T));
 #pragma unroll
-      for (int q = 0; q < W; ++q) {
-        if constexpr (sizeof(T) == 4) w[q] = elem_bits<T>(x[q], e);
-        else w[q] = elem_bits<T>(x[2 * q], e) | (elem_bits<T>(x[2 * q + 1], e) << 16);
-      }
-      // bytes [b, b + 4W) of tile row `row`; pieces of at most 16 bytes never
-      // straddle a 16-byte chunk, so each is placed by its chunk's swizzle
-      const int row = rv * VEC + e;
-      const int b = kg * KB * (int)sizeof(T);
-      char *rbase = (char *)(s + row * stride);
-      if constexpr (W == 1) {
-        *(uint32_t *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = w[0];
-      } else if constexpr (W == 2) {
-        *(u32x2 *)(rbase + lds_chunk(row, b >> 4) * 16 + (b & 15)) = u32x2{w[0], w[1]};
-      } else {
-#pragma unroll
-        for (int q = 0; q < W; q += 4)
-          *(u32x4 *)(rbase + lds_chunk(row, (b >> 4) + q / 4) * 16) = u32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
-      }
+    for (int j = q * KB / 4; j < (q + 1) * KB / 4; ++j) {
+      const char *base = (const char *)(p + (int64_t)(k0 + j) * ld + r0);
+      x[j] = *(const u32x4 *)(base + off);
     }
+  }
+  __device__ __forceinline__ void store_q(T *s, int stride, int tid, int q) const {
+    static_assert(VEC % 4 == 0, "quarters of the transposed writes");
+    const int kg = tid % NKG, rv = tid / NKG;
+#pragma unroll
+    for (int e = q * VEC / 4; e < (q + 1) * VEC / 4; ++e) store_e(s, stride, kg, rv, e);
   }
 };
 
 template <typename T, bool KC, int R, int BK, int NT> struct Loader;
 template <typename T, int R, int BK, int NT> struct Loader<T, true, R, BK, NT> : LoaderKC<T, R, BK, NT> {};
 template <typename T, int R, int BK, int NT> struct Loader<T, false, R, BK, NT> : LoaderMC<T, R, BK, NT> {};
+
+// ---- block -> output tile ---------------------------------------------------------
+// Consecutive blocks are dealt round-robin over the 8 XCDs; the remap gives
+// each XCD a contiguous run of tiles, which are then ordered in groups of 8
+// tile-rows so the A and B panels a group shares stay in that XCD's L2.
+__device__ __forceinline__ void tile_origin(const GemmParams &p, int BM, int BN, int &bm0, int &bn0) {
+  int bid = blockIdx.x;
+  const int total = p.tiles_m * p.tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * p.tiles_n;
+  const int first_m = (bid / per_group) * GROUP;
+  const int gsize = min(p.tiles_m - first_m, GROUP);
+  const int tm = first_m + (bid % per_group) % gsize;
+  const int tn = (bid % per_group) / gsize;
+  bm0 = tm * BM;
+  bn0 = tn * BN;
+}
+
+// ---- epilogue of one BM x BN tile ---------------------------------------------------
+// acc[i][j] holds the 16x16 block (wm0 + 16i, wn0 + 16j) of the tile, lane l
+// owning row l % 16, columns 4(l / 16) .. +3.  The tile is staged through LDS
+// in NPASS passes of BM / NPASS rows.
+template <int BM, int BN, int NT, int FM, int FN, int NPASS, int EUQ = 0>
+__device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x4 (&acc)[FM][FN], int tid, int wm0,
+                                           int wn0, int bm0, int bn0) {
+  const int lane = tid & 63;
+  constexpr int RP = BM / NPASS;
+  constexpr int CSTRIDE = BN + 4;  // floats per staged row (16-byte pad)
+  // The lane owning C[m][n..n+3] of each 16x16 fragment writes it
+  // to the staged tile in LDS; then all threads walk the staged rows, four
+  // consecutive columns per thread, so global stores are whole-row coalesced.
+  const EpiParams &e = p.ep;
+  const bool fast = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && e.c_vec && (!e.aux || e.aux_vec) &&
+                    (!e.res || e.res_vec) && (!e.pre || e.pre_vec) && (!e.bias || e.bias_vec);
+  float *cs = (float *)smem;
+  float *part = p.splits > 1 ? p.partial + (int64_t)blockIdx.z * p.M * p.N : nullptr;
+  const bool pvec = (p.N & 3) == 0;
+  // each thread owns one group of four columns and rows r0, r0 + RS, ...
+  constexpr int CG = BN / 4;
+  static_assert(NT % CG == 0, "threads must tile whole staged rows");
+  constexpr int RS = NT / CG;
+  constexpr int RPT = RP / RS;
+  // rows whose loads are issued together (fewer while a second pass still
+  // holds its accumulators in registers)
+  constexpr int EU = EUQ > 0 ? EUQ : (NPASS > 1 ? 2 : (RPT >= 4 ? 4 : RPT));
+  static_assert(RPT % EU == 0, "rows per thread must split into batches");
+  const int cg = tid % CG, r0 = tid / CG;
+  const int n = bn0 + cg * 4;
+  float bias[4];
+  epi_bias(e, n, fast, bias);
+  const bool bwd = e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD;
+  const void *xin = bwd ? e.aux : e.res;
+  const int xin_type = bwd ? e.aux_type : e.res_type;
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if (wm0 / RP == pass) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int row = wm0 - pass * RP + i * 16 + (lane & 15);
+          const int col = wn0 + j * 16 + (lane >> 4) * 4;
+          *(f32x4 *)(cs + row * CSTRIDE + col) = acc[i][j];
+        }
+    }
+    __syncthreads();
+    const int m_base = bm0 + pass * RP;
+    if (part != nullptr) {
+      // split-K: raw FP32 partial sums, stores only
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const int m = m_base + r0 + q * RS;
+        const f32x4 v = *(const f32x4 *)(cs + (r0 + q * RS) * CSTRIDE + cg * 4);
+        if (m < p.M && n < p.N) {
+          float *dst = part + (int64_t)m * p.N + n;
+          if (pvec && n + 3 < p.N) {
+            *(f32x4 *)dst = v;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (n + j < p.N) dst[j] = v[j];
+          }
+        }
+      }
+    } else if (fast && !(bwd && e.res)) {
+      const int xs = xin == nullptr ? 0 : (xin_type == GE_F32 ? 4 : 2);
+      if (e.c_type == GE_F32) {
+        if (xs == 0) epi_rows_fast<4, 0, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+        else if (xs == 2) epi_rows_fast<4, 2, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+        else epi_rows_fast<4, 4, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+      } else {
+        if (xs == 0) epi_rows_fast<2, 0, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+        else if (xs == 2) epi_rows_fast<2, 2, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+        else epi_rows_fast<2, 4, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+      }
+    } else {
+      // edge tiles and unaligned operands: checked element access
+#pragma unroll
+      for (int q0 = 0; q0 < RPT; q0 += EU) {
+        f32x4 v[EU];
+        float a[EU][4], r[EU][4];
+#pragma unroll
+        for (int u = 0; u < EU; ++u) {
+          const int rr = r0 + (q0 + u) * RS;
+          v[u] = *(const f32x4 *)(cs + rr * CSTRIDE + cg * 4);
+          epi_fetch(e, m_base + rr, n, false, a[u], r[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < EU; ++u) epi_apply(e, m_base + r0 + (q0 + u) * RS, n, v[u], bias, a[u], r[u], false);
+      }
+    }
+    __syncthreads();
+  }
+}
 
 // ---- the kernel ---------------------------------------------------------------
 template <typename T, int LAYOUT, int BM, int BN, int BK, int WGM, int WGN>
@@ -475,23 +697,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
   const int lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WGN) * WTM, wn0 = (wave % WGN) * WTN;
 
-  // block -> tile: spread consecutive tiles over one XCD, then group along M
-  int bid = blockIdx.x;
-  const int total = p.tiles_m * p.tiles_n;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  constexpr int GROUP = 8;
-  const int per_group = GROUP * p.tiles_n;
-  const int first_m = (bid / per_group) * GROUP;
-  const int gsize = min(p.tiles_m - first_m, GROUP);
-  const int tm = first_m + (bid % per_group) % gsize;
-  const int tn = (bid % per_group) / gsize;
-  const int bm0 = tm * BM, bn0 = tn * BN;
+  int bm0, bn0;
+  tile_origin(p, BM, BN, bm0, bn0);
 
   const int nk_total = (p.K + BK - 1) / BK;
   const int nk_full = p.K / BK;
   const int kt0 = blockIdx.z * p.ktiles_per_split;
   const int kt1 = min(nk_total, kt0 + p.ktiles_per_split);
-  const bool interior = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && p.a_vec && p.b_vec;
+  const bool interior = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && p.a_vec && p.b_vec && p.off32;
 
   const T *__restrict__ Ap = (const T *)p.A;
   const T *__restrict__ Bp = (const T *)p.B;
@@ -629,90 +842,204 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
     }
   }
 
-  // Epilogue: the lane owning C[m][n..n+3] of each 16x16 fragment writes it
-  // to the staged tile in LDS; then all threads walk the staged rows, four
-  // consecutive columns per thread, so global stores are whole-row coalesced.
-  const EpiParams &e = p.ep;
-  const bool fast = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && e.c_vec && (!e.aux || e.aux_vec) &&
-                    (!e.res || e.res_vec) && (!e.pre || e.pre_vec) && (!e.bias || e.bias_vec);
-  float *cs = (float *)smem;
-  float *part = p.splits > 1 ? p.partial + (int64_t)blockIdx.z * p.M * p.N : nullptr;
-  const bool pvec = (p.N & 3) == 0;
-  // each thread owns one group of four columns and rows r0, r0 + RS, ...
-  constexpr int CG = BN / 4;
-  static_assert(NT % CG == 0, "threads must tile whole staged rows");
-  constexpr int RS = NT / CG;
-  constexpr int RPT = RP / RS;
-  // rows whose loads are issued together (fewer while a second pass still
-  // holds its accumulators in registers)
-  constexpr int EU = NPASS > 1 ? 2 : (RPT >= 4 ? 4 : RPT);
-  static_assert(RPT % EU == 0, "rows per thread must split into batches");
-  const int cg = tid % CG, r0 = tid / CG;
-  const int n = bn0 + cg * 4;
-  float bias[4];
-  epi_bias(e, n, fast, bias);
-  const bool bwd = e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD;
-  const void *xin = bwd ? e.aux : e.res;
-  const int xin_type = bwd ? e.aux_type : e.res_type;
-  for (int pass = 0; pass < NPASS; ++pass) {
-    if (wm0 / RP == pass) {
+  store_tile<BM, BN, NT, FM, FN, NPASS>(p, smem, acc, tid, wm0, wn0, bm0, bn0);
+}
+
+// ---- 256x256 tile on four waves --------------------------------------------------
+// One wave per SIMD, each owning a 128x128 quarter of the tile, so every
+// fragment read from LDS feeds eight MFMAs (the 8-wave kernel's 64- or
+// 128-wide quarters feed four).  A k-tile of BK is two k-chunks.  While the
+// MFMAs of chunk 0 run, the wave reads the fragments of chunk 1, writes the
+// next k-tile (fetched into registers one step earlier) into the other LDS
+// buffer and fetches the k-tile after it; one barrier then separates those
+// writes from the reads of the next k-tile, whose chunk-0 fragments are read
+// while the MFMAs of chunk 1 run.  The steady-state step is straight-line
+// code with scheduling groups that interleave memory instructions with the
+// MFMAs, since a single wave per SIMD has no other wave to fill its gaps.
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, NT = 256;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int KCH = 4 * VEC;
+  constexpr int BK = 128 / (int)sizeof(T);  // 128-byte LDS rows
+  constexpr int STRIDE = BK;
+  constexpr int NC = BK / KCH;
+  static_assert(NC == 2, "two k-chunks per k-tile");
+  constexpr int FM = 8, FN = 8;
+  constexpr bool A_KC = (LAYOUT != GE_TN);
+  constexpr bool B_KC = (LAYOUT == GE_NT);
+  constexpr int NPASS = 2;
+  constexpr int OPER_BYTES = 2 * (BM + BN) * STRIDE * (int)sizeof(T);
+  constexpr int STAGE_BYTES = (BM / NPASS) * (BN + 4) * 4;
+  constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
+  static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget of one CU");
+  typedef typename Frag<T>::V V;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  T(*sA)[BM * STRIDE] = (T(*)[BM * STRIDE])smem;
+  T(*sB)[BN * STRIDE] = (T(*)[BN * STRIDE])(smem + 2 * BM * STRIDE * sizeof(T));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  int bm0, bn0;
+  tile_origin(p, BM, BN, bm0, bn0);
+  const int nk_total = (p.K + BK - 1) / BK;
+  const int nk_full = p.K / BK;
+  const int kt0 = blockIdx.z * p.ktiles_per_split;
+  const int kt1 = min(nk_total, kt0 + p.ktiles_per_split);
+  const bool interior = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && p.a_vec && p.b_vec && p.off32;
+  const T *__restrict__ Ap = (const T *)p.A;
+  const T *__restrict__ Bp = (const T *)p.B;
+
+  f32x4 acc[FM][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wm0 - pass * RP + i * 16 + (lane & 15);
-          const int col = wn0 + j * 16 + (lane >> 4) * 4;
-          *(f32x4 *)(cs + row * CSTRIDE + col) = acc[i][j];
-        }
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int koff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) koff[c] = lds_chunk(lane & 15, 4 * c + (lane >> 4)) * VEC;
+  const int arow = (wm0 + (lane & 15)) * STRIDE;
+  const int brow = (wn0 + (lane & 15)) * STRIDE;
+
+  // Operands are staged one k-chunk (KCH) at a time: chunk c of k-tile t
+  // occupies the 64-byte half c of the rows of LDS buffer t % 2, so the two
+  // buffers form a ring of four chunk slots.  Phase q multiplies chunk q,
+  // reads the fragments of chunk q+1, writes chunk q+2 (fetched two phases
+  // earlier into register set q % 2) and fetches chunk q+4 into that set; a
+  // barrier ends every phase.  Chunk q+2's slot last held chunk q-2, whose
+  // fragments were read in phase q-3, and chunk q+1 was written in phase q-1,
+  // so one barrier per phase orders every LDS write against its readers, and
+  // each phase writes half a k-tile instead of one phase writing all of it.
+  typedef Loader<T, A_KC, BM, KCH, NT> LA;
+  typedef Loader<T, B_KC, BN, KCH, NT> LB;
+  LA la0, la1;
+  LB lb0, lb1;
+  constexpr int QH = KCH * (int)sizeof(T) / 16;  // 16-byte chunks per k-chunk (4)
+  auto ld_any = [&](LA &la, LB &lb, int q) {  // chunk q = 2 * k-tile + c
+    const int k0 = q * KCH;
+    if (interior && (q >> 1) < nk_full) {
+      la.load_fast(Ap, p.lda, bm0, k0, tid);
+      lb.load_fast(Bp, p.ldb, bn0, k0, tid);
+    } else {
+      la.load_checked(Ap, p.lda, bm0, p.M, k0, p.K, p.a_vec, tid);
+      lb.load_checked(Bp, p.ldb, bn0, p.N, k0, p.K, p.b_vec, tid);
+    }
+  };
+  auto st_all = [&](const LA &la, const LB &lb, int q) {
+#pragma unroll
+    for (int i = 0; i < LA::NSTORE; ++i) la.store_piece(sA[(q >> 1) & 1], STRIDE, tid, i, (q & 1) * QH);
+#pragma unroll
+    for (int i = 0; i < LB::NSTORE; ++i) lb.store_piece(sB[(q >> 1) & 1], STRIDE, tid, i, (q & 1) * QH);
+  };
+  // fa: A fragments of the chunk being multiplied; row i's fragment of the
+  // next chunk replaces it as soon as row i's MFMAs are issued.  fb0 / fb1:
+  // B fragments of even / odd chunks.
+  V fa[FM], fb0[FN], fb1[FN];
+  auto read_a = [&](int q, int i) {
+    fa[i] = *(const V *)(sA[(q >> 1) & 1] + arow + i * 16 * STRIDE + koff[q & 1]);
+  };
+  auto read_b = [&](int q, V(&fb)[FN]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = *(const V *)(sB[(q >> 1) & 1] + brow + j * 16 * STRIDE + koff[q & 1]);
+  };
+  // generic phase: MFMAs of chunk q with fb, then (when there is one) the
+  // fragments of chunk q+1
+  auto phase_any = [&](V(&fb)[FN], V(&fb_next)[FN], int q, bool next) {
+    if (next) read_b(q + 1, fb_next);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) FragA<T>::mma(fb[j], fa[i], acc[i][j]);
+      if (next) read_a(q + 1, i);
+    }
+  };
+  // steady phase q: every MFMA is its own scheduling region carrying at most
+  // one memory instruction -- B reads of chunk q+1 in slots 0-7, the loads of
+  // chunk q+3 into the other register set (written in phase q-1) from slot 0
+  // (A even slots, B odd), the LDS writes of chunk q+2 from slot 24 (A) and
+  // 40 (B), and each row's A read right after its last MFMA.  A load thus
+  // precedes its LDS write by more than one phase.
+  auto phase_fast = [&](V(&fb)[FN], V(&fb_next)[FN], const LA &law, const LB &lbw, LA &lal, LB &lbl, int q) {
+    const int wb = ((q + 2) >> 1) & 1, wq = ((q + 2) & 1) * QH;
+    const int k3 = (q + 3) * KCH;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        FragA<T>::mma(fb[j], fa[i], acc[i][j]);
+        const int slot = i * FN + j;
+        if (i == 0) fb_next[j] = *(const V *)(sB[((q + 1) >> 1) & 1] + brow + j * 16 * STRIDE + koff[(q + 1) & 1]);
+        if ((slot & 1) == 0 && slot / 2 < LA::NLOAD) lal.load_piece(Ap, p.lda, bm0, k3, tid, slot / 2);
+        if ((slot & 1) == 1 && slot / 2 < LB::NLOAD) lbl.load_piece(Bp, p.ldb, bn0, k3, tid, slot / 2);
+        if (slot >= 24 && (slot & 1) == 0 && (slot - 24) / 2 < LA::NSTORE)
+          law.store_piece(sA[wb], STRIDE, tid, (slot - 24) / 2, wq);
+        if (slot >= 40 && (slot & 1) == 0 && (slot - 40) / 2 < LB::NSTORE)
+          lbw.store_piece(sB[wb], STRIDE, tid, (slot - 40) / 2, wq);
+        if (j == FN - 1) read_a(q + 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  const int q0 = 2 * kt0, q1 = 2 * kt1;  // chunk range of this block
+  int q = q0;
+  // steady state: chunks q+4 and q+5 exist and are full interior ones.  Its
+  // prologue issues the same unconditional loads as a loop step, so the
+  // loop entry carries the same outstanding-load pattern as the back edge
+  // and the compiler's waits before the LDS writes stay partial.
+  const int q_end = 2 * min(kt1, nk_full) - 5;
+  if (interior && q0 + 1 < q_end) {
+    la0.load_fast(Ap, p.lda, bm0, q0 * KCH, tid);
+    lb0.load_fast(Bp, p.ldb, bn0, q0 * KCH, tid);
+    la1.load_fast(Ap, p.lda, bm0, (q0 + 1) * KCH, tid);
+    lb1.load_fast(Bp, p.ldb, bn0, (q0 + 1) * KCH, tid);
+    st_all(la0, lb0, q0);
+    la0.load_fast(Ap, p.lda, bm0, (q0 + 2) * KCH, tid);
+    lb0.load_fast(Bp, p.ldb, bn0, (q0 + 2) * KCH, tid);
+    st_all(la1, lb1, q0 + 1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) read_a(q0, i);
+    read_b(q0, fb0);
+    for (; q < q_end; q += 2) {
+      phase_fast(fb0, fb1, la0, lb0, la1, lb1, q);
+      __syncthreads();
+      phase_fast(fb1, fb0, la1, lb1, la0, lb0, q + 1);
+      __syncthreads();
+    }
+    // the steady loop leaves chunk q+2 in set 0; the remaining phases also
+    // expect chunk q+3 in set 1
+    if (q + 3 < q1) ld_any(la1, lb1, q + 3);
+  } else if (q0 < q1) {
+    ld_any(la0, lb0, q0);
+    st_all(la0, lb0, q0);
+    ld_any(la1, lb1, q0 + 1);
+    st_all(la1, lb1, q0 + 1);
+    if (q0 + 2 < q1) ld_any(la0, lb0, q0 + 2);
+    if (q0 + 3 < q1) ld_any(la1, lb1, q0 + 3);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) read_a(q0, i);
+    read_b(q0, fb0);
+  }
+  // remaining phases (edge tiles, the last chunks, a partial k-tile)
+  for (; q < q1; q += 2) {
+    phase_any(fb0, fb1, q, q + 1 < q1);
+    if (q + 2 < q1) {
+      st_all(la0, lb0, q + 2);
+      if (q + 4 < q1) ld_any(la0, lb0, q + 4);
     }
     __syncthreads();
-    const int m_base = bm0 + pass * RP;
-    if (part != nullptr) {
-      // split-K: raw FP32 partial sums, stores only
-#pragma unroll
-      for (int q = 0; q < RPT; ++q) {
-        const int m = m_base + r0 + q * RS;
-        const f32x4 v = *(const f32x4 *)(cs + (r0 + q * RS) * CSTRIDE + cg * 4);
-        if (m < p.M && n < p.N) {
-          float *dst = part + (int64_t)m * p.N + n;
-          if (pvec && n + 3 < p.N) {
-            *(f32x4 *)dst = v;
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (n + j < p.N) dst[j] = v[j];
-          }
-        }
-      }
-    } else if (fast && !(bwd && e.res)) {
-      const int xs = xin == nullptr ? 0 : (xin_type == GE_F32 ? 4 : 2);
-      if (e.c_type == GE_F32) {
-        if (xs == 0) epi_rows_fast<4, 0, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else if (xs == 2) epi_rows_fast<4, 2, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else epi_rows_fast<4, 4, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-      } else {
-        if (xs == 0) epi_rows_fast<2, 0, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else if (xs == 2) epi_rows_fast<2, 2, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else epi_rows_fast<2, 4, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-      }
-    } else {
-      // edge tiles and unaligned operands: checked element access
-#pragma unroll
-      for (int q0 = 0; q0 < RPT; q0 += EU) {
-        f32x4 v[EU];
-        float a[EU][4], r[EU][4];
-#pragma unroll
-        for (int u = 0; u < EU; ++u) {
-          const int rr = r0 + (q0 + u) * RS;
-          v[u] = *(const f32x4 *)(cs + rr * CSTRIDE + cg * 4);
-          epi_fetch(e, m_base + rr, n, false, a[u], r[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < EU; ++u) epi_apply(e, m_base + r0 + (q0 + u) * RS, n, v[u], bias, a[u], r[u], false);
-      }
+    phase_any(fb1, fb0, q + 1, q + 2 < q1);
+    if (q + 3 < q1) {
+      st_all(la1, lb1, q + 3);
+      if (q + 5 < q1) ld_any(la1, lb1, q + 5);
     }
     __syncthreads();
   }
+  store_tile<BM, BN, NT, FM, FN, NPASS, 4>(p, smem, acc, tid, wm0, wn0, bm0, bn0);
 }
 
 // ---- launch plan and per-type launchers ---------------------------------------
@@ -726,8 +1053,14 @@ template <typename T, int LAYOUT>
 void launch_t(const Plan &pl, const GemmParams &gp, hipStream_t s) {
   dim3 grid(pl.tiles_m * pl.tiles_n, 1, pl.splits);
   constexpr int BK = sizeof(T) == 4 ? 32 : 64;
-  if (pl.bm == 256)
+  // 256x256: measured on 4096^3, the four-wave kernel is faster when an
+  // operand is transposed on its way into LDS (NN, TN), the eight-wave
+  // ping-pong kernel when both are k-contiguous (NT) and for short k ranges
+  // (split-K blocks of fewer than 16 k-tiles)
+  if (pl.bm == 256 && (LAYOUT == GE_NT || pl.kps < 16))
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 256, 256, BK, 2, 4>), grid, dim3(512), 0, s, gp);
+  else if (pl.bm == 256)
+    hipLaunchKernelGGL((gemm_w4_kernel<T, LAYOUT>), grid, dim3(256), 0, s, gp);
   else if (pl.bn == 16)
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 128, 16, BK, 4, 1>), grid, dim3(256), 0, s, gp);
   else if (pl.bm == 128)
