@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm4096", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB elementwise copy, the reference dispatch for "
+                         "scaling hardware byte counters (FETCH_SIZE / WRITE_SIZE) to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the path on a single MI355X "
@@ -174,6 +177,15 @@ def main():
             gemm4096[layout] = {"us": round(t * 1e3, 1), "tflops": round(tf, 1),
                                 "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
             del A, Bm, out
+
+    if args.copy_calibration:
+        # reads 256 MiB and writes 256 MiB; run it twice so one dispatch is warm
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

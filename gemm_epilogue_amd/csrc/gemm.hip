@@ -6,7 +6,10 @@
 
 namespace ge {
 
-// Sums split-K partials in split order and applies the epilogue.
+// Sums split-K partials in split order and applies the epilogue.  The loads
+// of eight splits are issued together (the sum is still taken in split
+// order), so the pass is bound by bandwidth rather than by one memory round
+// trip per split.
 __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p) {
   const int groups = (p.N + 3) >> 2;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -16,14 +19,34 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p) {
   const int64_t mn = (int64_t)p.M * p.N;
   const float *src = p.partial + (int64_t)m * p.N + n;
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  const bool vec = (n + 3 < p.N) && (p.N & 3) == 0;
-  for (int s = 0; s < p.splits; ++s) {
-    if (vec) {
-      v += *(const f32x4 *)(src + s * mn);
-    } else {
+  constexpr int U = 8;
+  if ((n + 3 < p.N) && (p.N & 3) == 0) {
+    int s = 0;
+    for (; s + U <= p.splits; s += U) {
+      f32x4 t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = *(const f32x4 *)(src + (int64_t)(s + u) * mn);
+#pragma unroll
+      for (int u = 0; u < U; ++u) v += t[u];
+    }
+    for (; s < p.splits; ++s) v += *(const f32x4 *)(src + (int64_t)s * mn);
+  } else {
+    int s = 0;
+    for (; s + U <= p.splits; s += U) {
+      float t[U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[u][q] = (n + q < p.N) ? src[(int64_t)(s + u) * mn + q] : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += t[u][q];
+    }
+    for (; s < p.splits; ++s) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (n + q < p.N) v[q] += src[s * mn + q];
+        if (n + q < p.N) v[q] += src[(int64_t)s * mn + q];
     }
   }
   float b[4], a[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f};
@@ -111,6 +134,13 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
   gp.b_vec = vec_aligned(a.B, a.ldb, es, 16);
   // the fast loads address up to 64 operand rows from one per-thread 32-bit offset
   gp.off32 = (a.lda * es * 64 < ((int64_t)1 << 31)) && (a.ldb * es * 64 < ((int64_t)1 << 31));
+  // clamped edge loads: 16-byte vectors must stay whole inside the rows of an
+  // operand stored along m / n (A of TN, B of NN and TN)
+  {
+    const int64_t v = 16 / es;
+    const bool a_mc = a.layout == GE_TN, b_mc = a.layout != GE_NT;
+    gp.clamp = gp.a_vec && gp.b_vec && a.M >= v && a.N >= v && (!a_mc || a.M % v == 0) && (!b_mc || a.N % v == 0);
+  }
   gp.tiles_m = pl.tiles_m;
   gp.tiles_n = pl.tiles_n;
   gp.ktiles_per_split = pl.kps;

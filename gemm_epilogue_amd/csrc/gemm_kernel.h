@@ -61,6 +61,7 @@ struct GemmParams {
   int M, N, K;
   int a_vec, b_vec;
   int off32;  // per-thread operand offsets of the fast loads fit in 31 bits
+  int clamp;  // edge tiles may use vector loads with clamped rows / columns
   int tiles_m, tiles_n;
   int ktiles_per_split;
   int splits;
@@ -368,6 +369,18 @@ template <typename T, int R, int BK, int NT> struct LoaderKC {
       }
     }
   }
+  // edge tiles of an aligned operand, full k-tile: rows past rmax re-read row
+  // rmax - 1; they only feed accumulator rows that are never stored
+  __device__ __forceinline__ void load_clamped(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
+                                               int tid) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + i * NT;
+      if (PART && v >= NVEC) continue;
+      const int row = min(r0 + v / VPR, rmax - 1);
+      r[i] = *(const u32x4 *)(p + (int64_t)row * ld + k0 + (v % VPR) * VEC);
+    }
+  }
   // single fast loads / LDS writes, for spreading them over MFMA work
   static constexpr int NLOAD = NV, NSTORE = NV;
   __device__ __forceinline__ void load_piece(const T *__restrict__ p, int64_t ld, int r0, int k0, int tid, int i) {
@@ -513,6 +526,16 @@ template <typename T, int R, int BK, int NT> struct LoaderMC {
     const int kg = tid % NKG, rv = tid / NKG;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) store_e(s, stride, kg, rv, e);
+  }
+  // edge tiles (rmax a multiple of VEC), full k-tile: vectors past rmax
+  // re-read the last one; they only feed accumulators that are never stored
+  __device__ __forceinline__ void load_clamped(const T *__restrict__ p, int64_t ld, int r0, int rmax, int k0,
+                                               int tid) {
+    if (PART && tid >= ACTIVE) return;
+    const int kg = tid % NKG, rv = tid / NKG;
+    const int col = min(r0 + rv * VEC, rmax - VEC);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) x[j] = *(const u32x4 *)(p + (int64_t)(k0 + kg * KB + j) * ld + col);
   }
   // single fast loads (k-row j) and transposed LDS writes (column e); every
   // write reads all KB loaded vectors, so a step's writes precede its loads
@@ -771,6 +794,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
       if (interior && kt < nk_full) {
         la.load_fast(Ap, p.lda, ar0, kt * BK, gt);
         lb.load_fast(Bp, p.ldb, br0, kt * BK, gt);
+      } else if (LAYOUT == GE_TN && p.clamp && kt < nk_full) {
+        // (NN and NT instances of this kernel have no registers to spare)
+        la.load_clamped(Ap, p.lda, ar0, p.M, kt * BK, gt);
+        lb.load_clamped(Bp, p.ldb, br0, p.N, kt * BK, gt);
       } else {
         la.load_checked(Ap, p.lda, ar0, p.M, kt * BK, p.K, p.a_vec, gt);
         lb.load_checked(Bp, p.ldb, br0, p.N, kt * BK, p.K, p.b_vec, gt);
@@ -818,6 +845,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
       if (interior && kt < nk_full) {
         la.load_fast(Ap, p.lda, bm0, kt * BK, tid);
         lb.load_fast(Bp, p.ldb, bn0, kt * BK, tid);
+      } else if (p.clamp && kt < nk_full) {
+        la.load_clamped(Ap, p.lda, bm0, p.M, kt * BK, tid);
+        lb.load_clamped(Bp, p.ldb, bn0, p.N, kt * BK, tid);
       } else {
         la.load_checked(Ap, p.lda, bm0, p.M, kt * BK, p.K, p.a_vec, tid);
         lb.load_checked(Bp, p.ldb, bn0, p.N, kt * BK, p.K, p.b_vec, tid);
@@ -922,6 +952,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
     if (interior && (q >> 1) < nk_full) {
       la.load_fast(Ap, p.lda, bm0, k0, tid);
       lb.load_fast(Bp, p.ldb, bn0, k0, tid);
+    } else if (p.clamp && (q >> 1) < nk_full) {
+      la.load_clamped(Ap, p.lda, bm0, p.M, k0, tid);
+      lb.load_clamped(Bp, p.ldb, bn0, p.N, k0, tid);
     } else {
       la.load_checked(Ap, p.lda, bm0, p.M, k0, p.K, p.a_vec, tid);
       lb.load_checked(Bp, p.ldb, bn0, p.N, k0, p.K, p.b_vec, tid);
