@@ -29,6 +29,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16/BF16 MFMA
+# HBM bytes per launch of that NN GEMM kernel (fwd1 and fwd2 launches in equal
+# numbers): FETCH_SIZE + WRITE_SIZE counter passes of rocprofv3 over this
+# script, scaled by the counters' reading for a plain copy of known size
+# (--copy-calibration), as listed in
+# profiles/mlp784-2048-2048-10_fp16_b4096_hbm_bytes.md.  Taken on the current
+# kernel; to be re-measured whenever the kernel changes.
+NN_TRAFFIC_BYTES = 63.63e6
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 DIMS = [784, 2048, 2048, 10]
 BATCH, LR, MU, N_BATCHES = 4096, 0.05, 0.9, 50
@@ -152,7 +159,8 @@ def main():
     nn_ms = event_time_ms(torch, fwd_nn, K) / K          # per pair of launches
     nn_tflops = f_nn / (nn_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(nn_tflops, 1), "peak": PEAK_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(nn_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(nn_tflops / PEAK_F16_TFLOPS, 4),
+                "traffic": NN_TRAFFIC_BYTES,
                 "kernel": "gemm_kernel<f16, NN, 128x128 tile> (fwd1 + fwd2 of the step)",
                 "avg_launch_us": round(nn_ms * 1e3 / 2, 2)}
 

@@ -572,14 +572,19 @@ template <typename T, bool KC, int R, int BK, int NT> struct Loader;
 template <typename T, int R, int BK, int NT> struct Loader<T, true, R, BK, NT> : LoaderKC<T, R, BK, NT> {};
 template <typename T, int R, int BK, int NT> struct Loader<T, false, R, BK, NT> : LoaderMC<T, R, BK, NT> {};
 
-// ---- block -> output tile ---------------------------------------------------------
-// Consecutive blocks are dealt round-robin over the 8 XCDs; the remap gives
-// each XCD a contiguous run of tiles, which are then ordered in groups of 8
-// tile-rows so the A and B panels a group shares stay in that XCD's L2.
-__device__ __forceinline__ void tile_origin(const GemmParams &p, int BM, int BN, int &bm0, int &bn0) {
-  int bid = blockIdx.x;
-  const int total = p.tiles_m * p.tiles_n;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+// ---- block -> (split, output tile) ---------------------------------------------
+// Blocks are dealt round-robin over the 8 XCDs in dispatch order (x fastest,
+// then the split index z).  The remap gives each XCD a contiguous run of the
+// split-major work list -- so with split-K an XCD works on one split -- and
+// tiles are ordered in groups of 8 tile-rows, so the A and B panels that an
+// XCD's blocks share stay in its L2.
+__device__ __forceinline__ void block_work(const GemmParams &p, int BM, int BN, int &bm0, int &bn0, int &split) {
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int total = tiles * p.splits;
+  int lin = blockIdx.x + tiles * blockIdx.z;
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  split = lin / tiles;
+  const int bid = lin - split * tiles;
   constexpr int GROUP = 8;
   const int per_group = GROUP * p.tiles_n;
   const int first_m = (bid / per_group) * GROUP;
@@ -596,7 +601,7 @@ __device__ __forceinline__ void tile_origin(const GemmParams &p, int BM, int BN,
 // in NPASS passes of BM / NPASS rows.
 template <int BM, int BN, int NT, int FM, int FN, int NPASS, int EUQ = 0>
 __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x4 (&acc)[FM][FN], int tid, int wm0,
-                                           int wn0, int bm0, int bn0) {
+                                           int wn0, int bm0, int bn0, int split) {
   const int lane = tid & 63;
   constexpr int RP = BM / NPASS;
   constexpr int CSTRIDE = BN + 4;  // floats per staged row (16-byte pad)
@@ -607,7 +612,7 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x
   const bool fast = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && e.c_vec && (!e.aux || e.aux_vec) &&
                     (!e.res || e.res_vec) && (!e.pre || e.pre_vec) && (!e.bias || e.bias_vec);
   float *cs = (float *)smem;
-  float *part = p.splits > 1 ? p.partial + (int64_t)blockIdx.z * p.M * p.N : nullptr;
+  float *part = p.splits > 1 ? p.partial + (int64_t)split * p.M * p.N : nullptr;
   const bool pvec = (p.N & 3) == 0;
   // each thread owns one group of four columns and rows r0, r0 + RS, ...
   constexpr int CG = BN / 4;
@@ -720,12 +725,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
   const int lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WGN) * WTM, wn0 = (wave % WGN) * WTN;
 
-  int bm0, bn0;
-  tile_origin(p, BM, BN, bm0, bn0);
+  int bm0, bn0, split;
+  block_work(p, BM, BN, bm0, bn0, split);
 
   const int nk_total = (p.K + BK - 1) / BK;
   const int nk_full = p.K / BK;
-  const int kt0 = blockIdx.z * p.ktiles_per_split;
+  const int kt0 = split * p.ktiles_per_split;
   const int kt1 = min(nk_total, kt0 + p.ktiles_per_split);
   const bool interior = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && p.a_vec && p.b_vec && p.off32;
 
@@ -872,7 +877,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
     }
   }
 
-  store_tile<BM, BN, NT, FM, FN, NPASS>(p, smem, acc, tid, wm0, wn0, bm0, bn0);
+  store_tile<BM, BN, NT, FM, FN, NPASS>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
 }
 
 // ---- 256x256 tile on four waves --------------------------------------------------
@@ -911,11 +916,11 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
-  int bm0, bn0;
-  tile_origin(p, BM, BN, bm0, bn0);
+  int bm0, bn0, split;
+  block_work(p, BM, BN, bm0, bn0, split);
   const int nk_total = (p.K + BK - 1) / BK;
   const int nk_full = p.K / BK;
-  const int kt0 = blockIdx.z * p.ktiles_per_split;
+  const int kt0 = split * p.ktiles_per_split;
   const int kt1 = min(nk_total, kt0 + p.ktiles_per_split);
   const bool interior = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && p.a_vec && p.b_vec && p.off32;
   const T *__restrict__ Ap = (const T *)p.A;
@@ -1072,7 +1077,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
     }
     __syncthreads();
   }
-  store_tile<BM, BN, NT, FM, FN, NPASS, 4>(p, smem, acc, tid, wm0, wn0, bm0, bn0);
+  store_tile<BM, BN, NT, FM, FN, NPASS, 4>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
 }
 
 // ---- launch plan and per-type launchers ---------------------------------------
