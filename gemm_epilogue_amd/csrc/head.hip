@@ -1,0 +1,299 @@
+// Fused output layer of the MLP step for narrow outputs (C <= 16 classes),
+// FP16 storage, for gfx950.
+//
+// "Capstone 5: train a network with your CUDA kernels": the last layer's
+// logits Z = H W + b ("The minimum model"), the stable softmax cross-entropy
+// and its gradient dZ ("Read the worked reference"), the bias gradient
+// db = sum_rows(dZ) and the masked input gradient dH = (dZ W^T) * [H > 0]
+// ("Work through the backward pass").  With ten classes each of these is a
+// GEMM or reduction only ten columns wide; as separate launches they are
+// bound by launch and memory latency, so one kernel computes them all from
+// one pass over H (the weight gradient dW = H^T dZ stays a GEMM).
+//
+// A prep kernel writes W (D x C, row-major) in the two layouts the MFMAs
+// read, zero-padded to 16 classes: W^T (16 x D) and W (D x 16), 128 KiB for
+// D = 2048, which stay in L2.  The head kernel then needs no LDS: a block is
+// one wave and takes 16 rows, and the loads of H are issued 16-32 at a time.
+//  * Z: v_mfma_f32_16x16x32_f16 over D in chunks of 32, the W^T fragment in
+//    the first operand slot, so lane l owns Z[row l%16][4(l/16) .. +3].
+//  * loss and G: the four lanes of a row (l, l^16, l^32, l^48) reduce the
+//    row maximum (lowest index on ties), the sum of the other terms and the
+//    label's term; the formulas are those of xent_rows_kernel.  G is rounded
+//    to FP16 once and that value is what every later use sees.
+//  * dH: per 16 hidden units h0.., v_mfma_f32_16x16x16_f16 with W[h][4q..]
+//    and the lane's own four G values gives lane l the four values
+//    dH[row l%16][h0 + 4(l/16) .. +3], masked by H of the same elements.
+//  * partial sums per block (in a fixed order): column sums of the rounded G
+//    and the sum of the row losses; the final kernel adds them in a fixed
+//    tree over the blocks.
+#include "common.h"
+
+namespace ge {
+
+namespace {
+
+constexpr int HEAD_ROWS = 16;   // rows per block (one wave)
+constexpr int HEAD_PART = 17;   // floats per block partial: 16 column sums + loss sum
+constexpr int HEAD_DMAX = 8192; // widest input (the W layouts stay in L2)
+
+typedef uint32_t hu32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t hu32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(half_t, (uint16_t)bits16);
+}
+
+}  // namespace
+
+// W (D x C) -> WT (16 x D) and WP (D x 16), classes C..15 zero
+__global__ __launch_bounds__(256) void mlp_head_prep_kernel(const half_t *__restrict__ W, int D, int C,
+                                                            half_t *__restrict__ WT, half_t *__restrict__ WP) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= D * 16) return;
+  const int k = i >> 4, c = i & 15;
+  const half_t v = c < C ? W[(int64_t)k * C + c] : (half_t)0.f;
+  WP[i] = v;
+  WT[(int64_t)c * D + k] = v;
+}
+
+__global__ __launch_bounds__(64) void mlp_head_kernel(const half_t *__restrict__ H, int B, int D,
+                                                      const half_t *__restrict__ WT,
+                                                      const half_t *__restrict__ WP, const float *__restrict__ bias,
+                                                      int C, const int32_t *__restrict__ labels, float gscale,
+                                                      float *__restrict__ Z, half_t *__restrict__ G,
+                                                      float *__restrict__ row_loss, half_t *__restrict__ dH,
+                                                      float *__restrict__ part) {
+  const int lane = threadIdx.x;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int row = blockIdx.x * HEAD_ROWS + r16;
+  const bool rok = row < B;
+  const half_t *hrow = H + (int64_t)min(row, B - 1) * D;
+
+  // ---- Z = H W (FP32 accumulation), lane: row r16, classes 4q .. 4q+3.
+  // Chunks of 32 along D, 16 chunks' loads per batch, two batches in flight.
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const half_t *wrow = WT + (int64_t)r16 * D + q * 8;
+    const half_t *hp = hrow + q * 8;
+    constexpr int U = 8;
+    f16x8 a0[U], a1[U], b0[U], b1[U];
+    auto load = [&](f16x8(&a)[U], f16x8(&b)[U], int k0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (k0 + 32 * u < D) {
+          a[u] = *(const f16x8 *)(hp + k0 + 32 * u);
+          b[u] = *(const f16x8 *)(wrow + k0 + 32 * u);
+        }
+    };
+    auto mma = [&](f16x8(&a)[U], f16x8(&b)[U], int k0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (k0 + 32 * u < D) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[u], a[u], acc, 0, 0, 0);
+    };
+    load(a0, b0, 0);
+    for (int k0 = 0; k0 < D; k0 += 64 * U) {
+      if (k0 + 32 * U < D) load(a1, b1, k0 + 32 * U);
+      mma(a0, b0, k0);
+      if (k0 + 32 * U < D) {
+        if (k0 + 64 * U < D) load(a0, b0, k0 + 64 * U);
+        mma(a1, b1, k0 + 32 * U);
+      }
+    }
+  }
+
+  // ---- stable softmax cross-entropy of the row, shared by its four lanes
+  float z[4];
+  float m = -INFINITY;
+  int mi = 0x7fffffff;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = 4 * q + t;
+    z[t] = c < C ? acc[t] + bias[c] : -INFINITY;
+    if (c < C && z[t] > m) {
+      m = z[t];
+      mi = c;
+    }
+  }
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float om = __shfl_xor(m, o, 64);
+    const int oi = __shfl_xor(mi, o, 64);
+    if (om > m || (om == m && oi < mi)) {
+      m = om;
+      mi = oi;
+    }
+  }
+  const int y = rok ? labels[row] : -1;
+  const bool yok = (unsigned)y < (unsigned)C;
+  float s_rest = 0.f, e_y = 0.f, z_y = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = 4 * q + t;
+    const float e = c < C ? expf(z[t] - m) : 0.f;
+    if (c < C && c != mi) s_rest += e;
+    if (c == y) {
+      e_y = e;
+      z_y = z[t];
+    }
+  }
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    s_rest += __shfl_xor(s_rest, o, 64);
+    e_y += __shfl_xor(e_y, o, 64);  // exactly one lane of the row holds it
+    z_y += __shfl_xor(z_y, o, 64);
+  }
+  const float l1p = log1pf(s_rest);
+  const float lse = m + l1p;
+  const float s = 1.f + s_rest;
+  const float s_noty = (y == mi) ? s_rest : s - e_y;
+  const float rl = yok ? (m - z_y) + l1p : NAN;
+
+  // G (rounded to FP16 once), Z and the row loss
+  half_t g16[4];
+  float gsum[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = 4 * q + t;
+    const float g = (c == y) ? -(s_noty / s) : expf(z[t] - lse);
+    g16[t] = (half_t)(c < C ? gscale * g : 0.f);
+    gsum[t] = rok ? (float)g16[t] : 0.f;
+  }
+  if (rok) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = 4 * q + t;
+      if (c < C) {
+        Z[(int64_t)row * C + c] = z[t];
+        G[(int64_t)row * C + c] = g16[t];
+      }
+    }
+    if (q == 0) row_loss[row] = rl;
+  }
+
+  // ---- block partials: column sums of G over the 16 rows, sum of row losses
+  {
+    float lsum = (rok && q == 0) ? rl : 0.f;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) gsum[t] += __shfl_xor(gsum[t], o, 64);
+      lsum += __shfl_xor(lsum, o, 64);
+    }
+    float *dst = part + (int64_t)blockIdx.x * HEAD_PART;
+    if (r16 == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[4 * q + t] = gsum[t];
+      if (q == 0) dst[16] = lsum;
+    }
+  }
+
+  // ---- dH = (G W^T) * [H > 0]; lane: row r16, hidden units h0 + 4q .. +3.
+  // The W and mask loads of 16 steps are issued together, two batches in
+  // flight.
+  {
+    const f16x4 gy = {g16[0], g16[1], g16[2], g16[3]};
+    half_t *drow = dH + (int64_t)row * D;
+    const half_t *hq = hrow + 4 * q;
+    const half_t *wq = WP + (int64_t)r16 * 16 + 4 * q;
+    constexpr int U = 16;
+    hu32x2 m0[U], m1[U];
+    f16x4 w0[U], w1[U];
+    auto load = [&](hu32x2(&hm)[U], f16x4(&wx)[U], int h00) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int h0 = h00 + 16 * u;
+        if (h0 < D) {
+          hm[u] = *(const hu32x2 *)(hq + h0);
+          wx[u] = *(const f16x4 *)(wq + (int64_t)h0 * 16);
+        }
+      }
+    };
+    auto compute = [&](hu32x2(&hm)[U], f16x4(&wx)[U], int h00) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int h0 = h00 + 16 * u;
+        if (h0 < D) {
+          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(wx[u], gy, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if (rok) {
+            f16x4 o;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t hb = (hm[u][t >> 1] >> (16 * (t & 1))) & 0xffffu;
+              o[t] = (half_t)(h2f(hb) > 0.f ? d[t] : 0.f);
+            }
+            *(f16x4 *)(drow + h0 + 4 * q) = o;
+          }
+        }
+      }
+    };
+    load(m0, w0, 0);
+    for (int h00 = 0; h00 < D; h00 += 32 * U) {
+      if (h00 + 16 * U < D) load(m1, w1, h00 + 16 * U);
+      compute(m0, w0, h00);
+      if (h00 + 16 * U < D) {
+        if (h00 + 32 * U < D) load(m0, w0, h00 + 32 * U);
+        compute(m1, w1, h00 + 16 * U);
+      }
+    }
+  }
+}
+
+// Block partials -> bias gradient (alpha * column sums) and mean loss.  Each
+// of the 17 sums has 32 threads: thread j adds blocks j, j+32, ... in order,
+// then a fixed butterfly over the 32 threads.
+__global__ __launch_bounds__(HEAD_PART * 32) void mlp_head_final_kernel(const float *__restrict__ part,
+                                                                         int nblocks, int B, int C, float alpha,
+                                                                         float *__restrict__ db,
+                                                                         float *__restrict__ loss) {
+  const int col = threadIdx.x >> 5, j = threadIdx.x & 31;
+  float s = 0.f;
+  int b = j;
+  for (; b + 32 * 7 < nblocks; b += 32 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(b + 32 * u) * HEAD_PART + col];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; b < nblocks; b += 32) s += part[(int64_t)b * HEAD_PART + col];
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (j == 0) {
+    if (col < C) db[col] = alpha * s;
+    if (col == 16) loss[0] = B > 0 ? s / (float)B : 0.f;
+  }
+}
+
+bool head_supported(int64_t B, int64_t D, int64_t C) {
+  return B >= 1 && C >= 1 && C <= 16 && D >= 32 && D <= HEAD_DMAX && D % 32 == 0;
+}
+
+// partials, then the two layouts of W (256-byte aligned)
+int64_t head_ws_bytes(int64_t B, int64_t D) {
+  const int64_t p = (((B + HEAD_ROWS - 1) / HEAD_ROWS) * HEAD_PART * 4 + 255) / 256 * 256;
+  return p + 2 * D * 16 * 2;
+}
+
+int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const float *bias, int64_t C,
+                const int32_t *labels, float gscale, float alpha, float *Z, half_t *G, float *row_loss,
+                half_t *dH, float *db, float *loss, void *ws, hipStream_t st) {
+  const int nblocks = (int)((B + HEAD_ROWS - 1) / HEAD_ROWS);
+  float *part = (float *)ws;
+  const int64_t p = ((int64_t)nblocks * HEAD_PART * 4 + 255) / 256 * 256;
+  half_t *WT = (half_t *)((char *)ws + p);
+  half_t *WP = WT + D * 16;
+  hipLaunchKernelGGL(mlp_head_prep_kernel, dim3((unsigned)((D * 16 + 255) / 256)), dim3(256), 0, st, W, (int)D,
+                     (int)C, WT, WP);
+  int s = launch_status("mlp head (prep)");
+  if (s != GE_OK) return s;
+  hipLaunchKernelGGL(mlp_head_kernel, dim3(nblocks), dim3(64), 0, st, H, (int)B, (int)D, (const half_t *)WT,
+                     (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part);
+  s = launch_status("mlp head");
+  if (s != GE_OK) return s;
+  hipLaunchKernelGGL(mlp_head_final_kernel, dim3(1), dim3(HEAD_PART * 32), 0, st, (const float *)part, nblocks,
+                     (int)B, (int)C, alpha, db, loss);
+  return launch_status("mlp head (final)");
+}
+
+}  // namespace ge

@@ -26,7 +26,16 @@ inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; 
 struct MlpLayout {
   std::vector<int64_t> h_off;  // H_1..H_{L-1}
   int64_t z_off, g_off, dh_off[2], loss_off, gemm_ws_off, gemm_ws, cs_ws_off, cs_ws, total;
+  bool head;  // the last layer runs as one fused kernel (mlp_head_kernel)
+  int64_t head_off;
 };
+
+// The fused output layer applies to FP16 storage, at least one hidden layer
+// and a narrow last layer (C <= 16) whose input width fits its LDS copy of W.
+bool use_head(const ge_mlp_desc *d, int64_t B) {
+  const int nl = d->n_layers;
+  return d->storage == GE_F16 && nl >= 2 && head_supported(B, d->dims[nl - 1], d->dims[nl]);
+}
 
 bool desc_ok(const ge_mlp_desc *d) {
   if (!d || d->n_layers < 1 || d->n_layers > 64 || !d->dims) return false;
@@ -71,6 +80,9 @@ MlpLayout layout_of(const ge_mlp_desc *d, int64_t B) {
   L.cs_ws_off = off;
   L.cs_ws = cws;
   off = align_up(off + cws);
+  L.head = use_head(d, B);
+  L.head_off = off;
+  if (L.head) off = align_up(off + head_ws_bytes(B, d->dims[d->n_layers - 1]));
   L.total = off;
   return L;
 }
@@ -183,8 +195,8 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   void *gws = L.gemm_ws ? ws + L.gemm_ws_off : nullptr;
   void *cws = L.cs_ws ? ws + L.cs_ws_off : nullptr;
 
-  // forward
-  for (int l = 1; l <= nl; ++l) {
+  // forward (with the fused head, the last layer's GEMM is part of it)
+  for (int l = 1; l <= (L.head ? nl - 1 : nl); ++l) {
     const bool last = l == nl;
     ge_gemm_args a = gemm_args(GE_NN, st, B, d[l], d[l - 1], hptr(l - 1), d[l - 1], wptr(l), d[l],
                                last ? (void *)Z : hptr(l), d[l], last ? GE_F32 : st);
@@ -197,7 +209,15 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   // loss and dZ ("G"): f32 plan scales by 1/B here, f16 plan in the dW / db epilogues
   const float gscale = f16 ? 1.f : 1.f / (float)B;
   const float alpha = f16 ? 1.f / (float)B : 1.f;
-  RUN(xent_launch(Z, B, d[nl], d[nl], labels, gscale, loss_out, row_loss, G, d[nl], st, nullptr, s));
+  if (L.head) {
+    // logits, loss, dZ, the last bias gradient and the first masked input
+    // gradient dH_{L-1} (into the first ping-pong buffer) in one pass
+    RUN(head_launch((const half_t *)hptr(nl - 1), B, d[nl - 1], (const half_t *)wptr(nl), buf->params + b_off[nl],
+                    d[nl], labels, gscale, alpha, Z, (half_t *)G, row_loss, (half_t *)(ws + L.dh_off[0]),
+                    buf->grads + b_off[nl], loss_out, ws + L.head_off, s));
+  } else {
+    RUN(xent_launch(Z, B, d[nl], d[nl], labels, gscale, loss_out, row_loss, G, d[nl], st, nullptr, s));
+  }
   // backward
   const void *Gl = G;
   int ping = 0;
@@ -208,8 +228,12 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
     a.workspace = gws;
     a.workspace_bytes = L.gemm_ws;
     RUN(gemm_launch(a, s));
-    RUN(colsum_launch(Gl, B, d[l], d[l], st, alpha, buf->grads + b_off[l], cws, L.cs_ws, s));
-    if (l > 1) {
+    const bool fused = L.head && l == nl;  // db and dH of this layer came from the head
+    if (!fused) RUN(colsum_launch(Gl, B, d[l], d[l], st, alpha, buf->grads + b_off[l], cws, L.cs_ws, s));
+    if (fused) {
+      Gl = ws + L.dh_off[ping];
+      ping ^= 1;
+    } else if (l > 1) {
       void *dH = ws + L.dh_off[ping];
       ge_gemm_args b = gemm_args(GE_NT, st, B, d[l - 1], d[l], Gl, d[l], wptr(l), d[l], dH, d[l - 1], st);
       b.act = GE_ACT_RELU_MASK_BWD;
