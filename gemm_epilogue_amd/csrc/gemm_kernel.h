@@ -880,10 +880,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
   store_tile<BM, BN, NT, FM, FN, NPASS>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
 }
 
-// ---- 256x256 tile on four waves --------------------------------------------------
-// One wave per SIMD, each owning a 128x128 quarter of the tile, so every
-// fragment read from LDS feeds eight MFMAs (the 8-wave kernel's 64- or
-// 128-wide quarters feed four).  A k-tile of BK is two k-chunks.  While the
+// ---- 256 x BN tile on four waves (BN = 256 or 128) ------------------------------------
+// One wave per SIMD, each owning a 128 x BN/2 quarter of the tile, so every A
+// fragment read from LDS feeds BN/32 MFMAs (eight for BN = 256, where the
+// 8-wave kernel's 64- or 128-wide quarters feed four).  A k-tile of BK is two k-chunks.  While the
 // MFMAs of chunk 0 run, the wave reads the fragments of chunk 1, writes the
 // next k-tile (fetched into registers one step earlier) into the other LDS
 // buffer and fetches the k-tile after it; one barrier then separates those
@@ -891,16 +891,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
 // while the MFMAs of chunk 1 run.  The steady-state step is straight-line
 // code with scheduling groups that interleave memory instructions with the
 // MFMAs, since a single wave per SIMD has no other wave to fill its gaps.
-template <typename T, int LAYOUT>
+template <typename T, int LAYOUT, int BN>
 __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256, NT = 256;
+  constexpr int BM = 256, NT = 256;
+  static_assert(BN == 256 || BN == 128, "tile width");
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KCH = 4 * VEC;
   constexpr int BK = 128 / (int)sizeof(T);  // 128-byte LDS rows
   constexpr int STRIDE = BK;
   constexpr int NC = BK / KCH;
   static_assert(NC == 2, "two k-chunks per k-tile");
-  constexpr int FM = 8, FN = 8;
+  constexpr int FM = 8, FN = BN / 32;
   constexpr bool A_KC = (LAYOUT != GE_TN);
   constexpr bool B_KC = (LAYOUT == GE_NT);
   constexpr int NPASS = 2;
@@ -915,7 +916,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * (BN / 2);
   int bm0, bn0, split;
   block_work(p, BM, BN, bm0, bn0, split);
   const int nk_total = (p.K + BK - 1) / BK;
@@ -994,11 +995,16 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
     }
   };
   // steady phase q: every MFMA is its own scheduling region carrying at most
-  // one memory instruction -- B reads of chunk q+1 in slots 0-7, the loads of
-  // chunk q+3 into the other register set (written in phase q-1) from slot 0
-  // (A even slots, B odd), the LDS writes of chunk q+2 from slot 24 (A) and
-  // 40 (B), and each row's A read right after its last MFMA.  A load thus
-  // precedes its LDS write by more than one phase.
+  // one memory instruction -- B reads of chunk q+1 in row 0, then the loads
+  // of chunk q+3 into the other register set (written in phase q-1), one per
+  // slot from slot 0 (A first), then the LDS writes of chunk q+2 spread over
+  // the second part of the phase, and each row's A read right after its last
+  // MFMA.  A load thus precedes its LDS write by more than one phase.
+  constexpr int NSLOT = FM * FN;
+  constexpr int NLD = LA::NLOAD + LB::NLOAD, NST = LA::NSTORE + LB::NSTORE;
+  constexpr int W0 = NSLOT * 3 / 8;
+  constexpr int WS = (NSLOT - W0) / NST > 0 ? (NSLOT - W0) / NST : 1;
+  static_assert(NLD <= W0 && W0 + WS * (NST - 1) < NSLOT, "memory slots must fit the phase");
   auto phase_fast = [&](V(&fb)[FN], V(&fb_next)[FN], const LA &law, const LB &lbw, LA &lal, LB &lbl, int q) {
     const int wb = ((q + 2) >> 1) & 1, wq = ((q + 2) & 1) * QH;
     const int k3 = (q + 3) * KCH;
@@ -1009,12 +1015,13 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
         FragA<T>::mma(fb[j], fa[i], acc[i][j]);
         const int slot = i * FN + j;
         if (i == 0) fb_next[j] = *(const V *)(sB[((q + 1) >> 1) & 1] + brow + j * 16 * STRIDE + koff[(q + 1) & 1]);
-        if ((slot & 1) == 0 && slot / 2 < LA::NLOAD) lal.load_piece(Ap, p.lda, bm0, k3, tid, slot / 2);
-        if ((slot & 1) == 1 && slot / 2 < LB::NLOAD) lbl.load_piece(Bp, p.ldb, bn0, k3, tid, slot / 2);
-        if (slot >= 24 && (slot & 1) == 0 && (slot - 24) / 2 < LA::NSTORE)
-          law.store_piece(sA[wb], STRIDE, tid, (slot - 24) / 2, wq);
-        if (slot >= 40 && (slot & 1) == 0 && (slot - 40) / 2 < LB::NSTORE)
-          lbw.store_piece(sB[wb], STRIDE, tid, (slot - 40) / 2, wq);
+        if (slot < LA::NLOAD) lal.load_piece(Ap, p.lda, bm0, k3, tid, slot);
+        else if (slot < NLD) lbl.load_piece(Bp, p.ldb, bn0, k3, tid, slot - LA::NLOAD);
+        if (slot >= W0 && (slot - W0) % WS == 0) {
+          const int w = (slot - W0) / WS;
+          if (w < LA::NSTORE) law.store_piece(sA[wb], STRIDE, tid, w, wq);
+          else if (w < NST) lbw.store_piece(sB[wb], STRIDE, tid, w - LA::NSTORE, wq);
+        }
         if (j == FN - 1) read_a(q + 1, i);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1082,7 +1089,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
 
 // ---- launch plan and per-type launchers ---------------------------------------
 struct Plan {
-  int bm, bn;  // tile: 256x256, 128x128, 64x64, or 128x16 for N <= 16
+  int bm, bn;  // tile: 256x256, 256x128, 128x128, 64x64, or 128x16 for N <= 16
   int BK;
   int tiles_m, tiles_n, nk, splits, kps;
 };
@@ -1095,10 +1102,12 @@ void launch_t(const Plan &pl, const GemmParams &gp, hipStream_t s) {
   // operand is transposed on its way into LDS (NN, TN), the eight-wave
   // ping-pong kernel when both are k-contiguous (NT) and for short k ranges
   // (split-K blocks of fewer than 16 k-tiles)
-  if (pl.bm == 256 && (LAYOUT == GE_NT || pl.kps < 16))
+  if (pl.bm == 256 && pl.bn == 128)
+    hipLaunchKernelGGL((gemm_w4_kernel<T, LAYOUT, 128>), grid, dim3(256), 0, s, gp);
+  else if (pl.bm == 256 && (LAYOUT == GE_NT || pl.kps < 16))
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 256, 256, BK, 2, 4>), grid, dim3(512), 0, s, gp);
   else if (pl.bm == 256)
-    hipLaunchKernelGGL((gemm_w4_kernel<T, LAYOUT>), grid, dim3(256), 0, s, gp);
+    hipLaunchKernelGGL((gemm_w4_kernel<T, LAYOUT, 256>), grid, dim3(256), 0, s, gp);
   else if (pl.bn == 16)
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, 128, 16, BK, 4, 1>), grid, dim3(256), 0, s, gp);
   else if (pl.bm == 128)

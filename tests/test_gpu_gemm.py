@@ -39,11 +39,11 @@ def _tol(fmt):
 
 
 # includes narrow outputs (N <= 16: 128x16 tiles with short K splits), a
-# long-K shape that takes 256x256 tiles with split-K, and aligned ragged
-# shapes whose edge tiles take clamped vector loads
+# long-K shape that takes 256x256 tiles with split-K, aligned ragged shapes
+# whose edge tiles take clamped vector loads, and one that takes 256x128 tiles
 RAGGED = [(1, 1, 1), (15, 17, 63), (65, 130, 100), (200, 72, 784), (130, 257, 129),
           (1800, 1800, 130), (96, 80, 3000), (300, 10, 1000), (33, 1, 70), (4096, 16, 2048),
-          (1000, 700, 8200), (776, 264, 1000)]
+          (1000, 700, 8200), (776, 264, 1000), (3000, 2000, 1600)]
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16", "f32"])
