@@ -29,13 +29,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16/BF16 MFMA
-# HBM bytes per launch of that NN GEMM kernel (fwd1 and fwd2 launches in equal
-# numbers): FETCH_SIZE + WRITE_SIZE counter passes of rocprofv3 over this
-# script, scaled by the counters' reading for a plain copy of known size
-# (--copy-calibration), as listed in
-# profiles/mlp784-2048-2048-10_fp16_b4096_hbm_bytes.md.  Taken on the current
-# kernel; to be re-measured whenever the kernel changes.
-NN_TRAFFIC_BYTES = 63.63e6
+# HBM bytes per launch of the roofline kernel (the fwd2 launch below):
+# FETCH_SIZE + WRITE_SIZE counter passes of rocprofv3 over this script, scaled
+# by the counters' reading for a plain copy of known size (--copy-calibration),
+# as listed in profiles/mlp784-2048-2048-10_fp16_b4096_hbm_bytes.md.  Taken on
+# the current kernel; to be re-measured whenever the kernel changes.
+NN_TRAFFIC_BYTES = 101.19e6
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 DIMS = [784, 2048, 2048, 10]
 BATCH, LR, MU, N_BATCHES = 4096, 0.05, 0.9, 50
@@ -137,32 +136,30 @@ def main():
     flops_step = mlp_flops_per_sample(DIMS) * BATCH
     loss = float(tr.loss.item())
 
-    # ---- dominant kernel: the NN GEMM-epilogue launches of the forward pass
-    # (fwd1 784->2048 and fwd2 2048->2048 share one kernel), replayed with the
+    # ---- dominant kernel: the 256x128 four-wave GEMM-epilogue kernel, which
+    # runs the step's two 4096x2048x2048 GEMMs (forward fwd2 and the masked
+    # dgrad); its forward launch (H2 = relu(H1 W2 + b2)) is replayed with the
     # step's own operands on the same stream and timed with HIP events.
     views = tr.workspace_views(BATCH)
     H1, H2 = views["H"]
     lowp = tr.params_lowp
     o1 = 784 * 2048 + 2048
-    W1 = lowp[:784 * 2048].view(784, 2048)
-    b1 = tr.params[784 * 2048:o1]
     W2 = lowp[o1:o1 + 2048 * 2048].view(2048, 2048)
     b2 = tr.params[o1 + 2048 * 2048:o1 + 2048 * 2048 + 2048]
-    f_nn = 2 * BATCH * 2048 * (784 + 2048)
+    f_nn = 2 * BATCH * 2048 * 2048
 
-    def fwd_nn(i):
-        ge.gemm_bias_act(Xs[i % nb], W1, "NN", bias=b1, act="relu", out=H1)
+    def fwd2(i):
         ge.gemm_bias_act(H1, W2, "NN", bias=b2, act="relu", out=H2)
 
     for i in range(3):
-        fwd_nn(i)
-    nn_ms = event_time_ms(torch, fwd_nn, K) / K          # per pair of launches
+        fwd2(i)
+    nn_ms = event_time_ms(torch, fwd2, K) / K
     nn_tflops = f_nn / (nn_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(nn_tflops, 1), "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(nn_tflops / PEAK_F16_TFLOPS, 4),
                 "traffic": NN_TRAFFIC_BYTES,
-                "kernel": "gemm_kernel<f16, NN, 128x128 tile> (fwd1 + fwd2 of the step)",
-                "avg_launch_us": round(nn_ms * 1e3 / 2, 2)}
+                "kernel": "gemm_w4_kernel<f16, NN, 256x128 tile> (fwd2 of the step, 4096x2048x2048)",
+                "avg_launch_us": round(nn_ms * 1e3, 2)}
 
     # ---- standalone 4096^3 GEMM + bias + ReLU epilogue, three layouts ------
     gemm4096 = None
