@@ -55,10 +55,58 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p) {
   epi_apply(p.ep, m, n, v, b, a, r, false);
 }
 
+// Many splits over a small output (the narrow weight gradient: 32 splits of
+// a 2048 x 10 tile): eight lanes per group of four columns, lane u adding
+// splits u, u+8, ... in order, then a fixed butterfly over the eight lanes,
+// so the pass takes one or two memory round trips instead of one per split.
+__global__ __launch_bounds__(256) void splitk_finish_wide_kernel(GemmParams p) {
+  const int groups = (p.N + 3) >> 2;
+  const int64_t items = (int64_t)p.M * groups;
+  const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+  const int u = threadIdx.x & 7;
+  const bool live = g < items;
+  const int m = live ? (int)(g / groups) : 0;
+  const int n = live ? (int)(g % groups) * 4 : 0;
+  const int64_t mn = (int64_t)p.M * p.N;
+  const float *src = p.partial + (int64_t)m * p.N + n;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    int s = u;
+    for (; s + 8 * 3 < p.splits; s += 8 * 4) {
+      float t[4][4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[w][q] = (n + q < p.N) ? src[(int64_t)(s + 8 * w) * mn + q] : 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += t[w][q];
+    }
+    for (; s < p.splits; s += 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (n + q < p.N) v[q] += src[(int64_t)s * mn + q];
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += __shfl_xor(v[q], o, 64);
+  }
+  if (!live || u != 0) return;
+  const f32x4 acc = {v[0], v[1], v[2], v[3]};
+  float b[4], a[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f};
+  epi_bias(p.ep, n, false, b);
+  epi_fetch(p.ep, m, n, false, a, r);
+  epi_apply(p.ep, m, n, acc, b, a, r, false);
+}
+
 // ---- host launcher --------------------------------------------------------------
 namespace {
 
 int64_t ntiles(int64_t M, int64_t N, int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); }
+int64_t t256_128(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 127) / 128); }
 
 Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   Plan pl;
@@ -80,7 +128,7 @@ Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   } else if (split_k < 1 && nk >= 48 && t256 * std::min<int64_t>(nk / 8, 64) >= 192) {
     pl.bm = pl.bn = 256;
     s = (int)std::min<int64_t>({(256 + t256 - 1) / t256, nk / 8, 64});
-  } else if (split_k < 1 && ((M + 255) / 256) * ((N + 127) / 128) >= 192 && nk >= 24) {
+  } else if (split_k < 1 && t256_128(M, N) >= 192 && nk >= 24) {
     // 256x128 on four waves: less LDS traffic per MFMA than 128x128; measured
     // faster once the k loop is long (slower at 13 k-tiles)
     pl.bm = 256;
@@ -194,7 +242,10 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
   int st = launch_status("gemm_bias_act");
   if (st != GE_OK || pl.splits <= 1) return st;
   const int64_t items = a.M * ((a.N + 3) / 4);
-  hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, gp);
+  if (items < (64 << 10) && pl.splits >= 8)
+    hipLaunchKernelGGL(splitk_finish_wide_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, gp);
+  else
+    hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, gp);
   return launch_status("gemm_bias_act (split-K finish)");
 }
 
