@@ -12,8 +12,11 @@
 //
 // A prep kernel writes W (D x C, row-major) in the two layouts the MFMAs
 // read, zero-padded to 16 classes: W^T (16 x D) and W (D x 16), 128 KiB for
-// D = 2048, which stay in L2.  The head kernel then needs no LDS: a block is
-// one wave and takes 16 rows, and the loads of H are issued 16-32 at a time.
+// D = 2048, which stay in L2.  A block of four waves takes 16 rows and splits
+// D four ways: each wave accumulates its quarter of the logits, the quarters
+// are added through LDS in wave order (so every wave holds the same logits
+// and computes the same loss and G), and each wave then forms dH for its own
+// quarter of the hidden units.  H is read once.
 //  * Z: v_mfma_f32_16x16x32_f16 over D in chunks of 32, the W^T fragment in
 //    the first operand slot, so lane l owns Z[row l%16][4(l/16) .. +3].
 //  * loss and G: the four lanes of a row (l, l^16, l^32, l^48) reduce the
@@ -32,9 +35,9 @@ namespace ge {
 
 namespace {
 
-constexpr int HEAD_ROWS = 16;   // rows per block (one wave)
+constexpr int HEAD_ROWS = 16;   // rows per block (four waves splitting D)
 constexpr int HEAD_PART = 17;   // floats per block partial: 16 column sums + loss sum
-constexpr int HEAD_DMAX = 8192; // widest input (the W layouts stay in L2)
+constexpr int HEAD_DMAX = 2048; // widest input (a wave keeps the ReLU mask of its quarter in 4 registers)
 
 typedef uint32_t hu32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t hu32x4 __attribute__((ext_vector_type(4)));
@@ -56,51 +59,80 @@ __global__ __launch_bounds__(256) void mlp_head_prep_kernel(const half_t *__rest
   WT[(int64_t)c * D + k] = v;
 }
 
-__global__ __launch_bounds__(64) void mlp_head_kernel(const half_t *__restrict__ H, int B, int D,
+__global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict__ H, int B, int D,
                                                       const half_t *__restrict__ WT,
                                                       const half_t *__restrict__ WP, const float *__restrict__ bias,
                                                       int C, const int32_t *__restrict__ labels, float gscale,
                                                       float *__restrict__ Z, half_t *__restrict__ G,
                                                       float *__restrict__ row_loss, half_t *__restrict__ dH,
                                                       float *__restrict__ part) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
+  __shared__ f32x4 red[4][64];
 
   const int row = blockIdx.x * HEAD_ROWS + r16;
   const bool rok = row < B;
   const half_t *hrow = H + (int64_t)min(row, B - 1) * D;
 
   // ---- Z = H W (FP32 accumulation), lane: row r16, classes 4q .. 4q+3.
-  // Chunks of 32 along D, 16 chunks' loads per batch, two batches in flight.
+  // Wave w takes chunks w*nch .. (w+1)*nch - 1 of 32 units.  In each chunk
+  // lane q supplies units 8q .. 8q+7 -- the units it owns in dH below -- so
+  // the ReLU mask [H > 0] is kept here as bits (8 per chunk).  The wave's
+  // chunks are loaded 8 at a time, two batches in flight; the loops are
+  // unrolled over the widest D so the mask bits stay in registers.
+  constexpr int NCH = HEAD_DMAX / 128;  // chunks per wave at the widest D
+  const int nch = D / 128;
+  const int cbase = wave * nch;
+  uint32_t mb[NCH / 4];
+#pragma unroll
+  for (int i = 0; i < NCH / 4; ++i) mb[i] = 0u;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   {
-    const half_t *wrow = WT + (int64_t)r16 * D + q * 8;
-    const half_t *hp = hrow + q * 8;
+    const half_t *wrow = WT + (int64_t)r16 * D + q * 8 + 32 * cbase;
+    const half_t *hp = hrow + q * 8 + 32 * cbase;
     constexpr int U = 8;
-    f16x8 a0[U], a1[U], b0[U], b1[U];
-    auto load = [&](f16x8(&a)[U], f16x8(&b)[U], int k0) {
+    hu32x4 av[2][U], bv[2][U];
+    auto load = [&](int bf, int c0) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (k0 + 32 * u < D) {
-          a[u] = *(const f16x8 *)(hp + k0 + 32 * u);
-          b[u] = *(const f16x8 *)(wrow + k0 + 32 * u);
+        if (c0 + u < nch) {
+          av[bf][u] = *(const hu32x4 *)(hp + 32 * (c0 + u));
+          bv[bf][u] = *(const hu32x4 *)(wrow + 32 * (c0 + u));
         }
     };
-    auto mma = [&](f16x8(&a)[U], f16x8(&b)[U], int k0) {
+    auto mma = [&](int bf, int c0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (k0 + 32 * u < D) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[u], a[u], acc, 0, 0, 0);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u;
+        if (c < nch) {
+          const hu32x4 a4 = av[bf][u];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, bv[bf][u]),
+                                                       __builtin_bit_cast(f16x8, a4), acc, 0, 0, 0);
+          uint32_t bits = 0u;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t hb = (a4[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+            bits |= (h2f(hb) > 0.f ? 1u : 0u) << t;
+          }
+          mb[c >> 2] |= bits << (8 * (c & 3));
+        }
+      }
     };
-    load(a0, b0, 0);
-    for (int k0 = 0; k0 < D; k0 += 64 * U) {
-      if (k0 + 32 * U < D) load(a1, b1, k0 + 32 * U);
-      mma(a0, b0, k0);
-      if (k0 + 32 * U < D) {
-        if (k0 + 64 * U < D) load(a0, b0, k0 + 64 * U);
-        mma(a1, b1, k0 + 32 * U);
+    load(0, 0);
+#pragma unroll
+    for (int c0 = 0; c0 < NCH; c0 += 2 * U) {
+      if (c0 + U < nch) load(1, c0 + U);
+      mma(0, c0);
+      if (c0 + U < nch) {
+        if (c0 + 2 * U < nch) load(0, c0 + 2 * U);
+        mma(1, c0 + U);
       }
     }
   }
+  // the four quarters, added in wave order
+  red[wave][lane] = acc;
+  __syncthreads();
+  acc = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 
   // ---- stable softmax cross-entropy of the row, shared by its four lanes
   float z[4];
@@ -159,7 +191,7 @@ __global__ __launch_bounds__(64) void mlp_head_kernel(const half_t *__restrict__
     g16[t] = (half_t)(c < C ? gscale * g : 0.f);
     gsum[t] = rok ? (float)g16[t] : 0.f;
   }
-  if (rok) {
+  if (rok && wave == 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int c = 4 * q + t;
@@ -181,59 +213,64 @@ __global__ __launch_bounds__(64) void mlp_head_kernel(const half_t *__restrict__
       lsum += __shfl_xor(lsum, o, 64);
     }
     float *dst = part + (int64_t)blockIdx.x * HEAD_PART;
-    if (r16 == 0) {
+    if (r16 == 0 && wave == 0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) dst[4 * q + t] = gsum[t];
       if (q == 0) dst[16] = lsum;
     }
   }
 
-  // ---- dH = (G W^T) * [H > 0]; lane: row r16, hidden units h0 + 4q .. +3.
-  // The W and mask loads of 16 steps are issued together, two batches in
-  // flight.
+  // ---- dH = (G W^T) * [H > 0] per chunk c of 32 units, in two 16x16x16
+  // MFMAs whose 16 W rows are units 32c + 8(i/4) + (i%4) (first) and
+  // 32c + 8(i/4) + 4 + (i%4) (second) for output row i; lane l then holds
+  // units 32c + 8q .. 8q+7 of row r16 -- one 16-byte store, masked by the
+  // chunk's bits.  The W loads of 8 chunks are issued together, two batches
+  // in flight.
   {
     const f16x4 gy = {g16[0], g16[1], g16[2], g16[3]};
-    half_t *drow = dH + (int64_t)row * D;
-    const half_t *hq = hrow + 4 * q;
-    const half_t *wq = WP + (int64_t)r16 * 16 + 4 * q;
-    constexpr int U = 16;
-    hu32x2 m0[U], m1[U];
-    f16x4 w0[U], w1[U];
-    auto load = [&](hu32x2(&hm)[U], f16x4(&wx)[U], int h00) {
+    half_t *drow = dH + (int64_t)row * D + 8 * q + 32 * cbase;
+    const int hl = 8 * (r16 >> 2) + (r16 & 3);  // unit of W row r16 in the first MFMA
+    const half_t *wq = WP + (int64_t)(hl + 32 * cbase) * 16 + 4 * q;
+    constexpr int U = 8;
+    f16x4 w0[2][U], w1[2][U];
+    auto load = [&](int bf, int c0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int h0 = h00 + 16 * u;
-        if (h0 < D) {
-          hm[u] = *(const hu32x2 *)(hq + h0);
-          wx[u] = *(const f16x4 *)(wq + (int64_t)h0 * 16);
+      for (int u = 0; u < U; ++u)
+        if (c0 + u < nch) {
+          const half_t *w = wq + (int64_t)(c0 + u) * 32 * 16;
+          w0[bf][u] = *(const f16x4 *)w;
+          w1[bf][u] = *(const f16x4 *)(w + 4 * 16);
         }
-      }
     };
-    auto compute = [&](hu32x2(&hm)[U], f16x4(&wx)[U], int h00) {
+    auto compute = [&](int bf, int c0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int h0 = h00 + 16 * u;
-        if (h0 < D) {
-          const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(wx[u], gy, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const int c = c0 + u;
+        if (c < nch) {
+          const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x16f16(w0[bf][u], gy, z0, 0, 0, 0);
+          const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x16f16(w1[bf][u], gy, z0, 0, 0, 0);
+          const uint32_t bits = (mb[c >> 2] >> (8 * (c & 3))) & 0xffu;
           if (rok) {
-            f16x4 o;
+            f16x8 o;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              const uint32_t hb = (hm[u][t >> 1] >> (16 * (t & 1))) & 0xffffu;
-              o[t] = (half_t)(h2f(hb) > 0.f ? d[t] : 0.f);
+              o[t] = (half_t)(((bits >> t) & 1u) ? d0[t] : 0.f);
+              o[4 + t] = (half_t)(((bits >> (4 + t)) & 1u) ? d1[t] : 0.f);
             }
-            *(f16x4 *)(drow + h0 + 4 * q) = o;
+            *(f16x8 *)(drow + 32 * c) = o;
           }
         }
       }
     };
-    load(m0, w0, 0);
-    for (int h00 = 0; h00 < D; h00 += 32 * U) {
-      if (h00 + 16 * U < D) load(m1, w1, h00 + 16 * U);
-      compute(m0, w0, h00);
-      if (h00 + 16 * U < D) {
-        if (h00 + 32 * U < D) load(m0, w0, h00 + 32 * U);
-        compute(m1, w1, h00 + 16 * U);
+    load(0, 0);
+#pragma unroll
+    for (int c0 = 0; c0 < NCH; c0 += 2 * U) {
+      if (c0 + U < nch) load(1, c0 + U);
+      compute(0, c0);
+      if (c0 + U < nch) {
+        if (c0 + 2 * U < nch) load(0, c0 + 2 * U);
+        compute(1, c0 + U);
       }
     }
   }
@@ -266,7 +303,7 @@ __global__ __launch_bounds__(HEAD_PART * 32) void mlp_head_final_kernel(const fl
 }
 
 bool head_supported(int64_t B, int64_t D, int64_t C) {
-  return B >= 1 && C >= 1 && C <= 16 && D >= 32 && D <= HEAD_DMAX && D % 32 == 0;
+  return B >= 1 && C >= 1 && C <= 16 && D >= 128 && D <= HEAD_DMAX && D % 128 == 0;
 }
 
 // partials, then the two layouts of W (256-byte aligned)
@@ -287,7 +324,7 @@ int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const fl
                      (int)C, WT, WP);
   int s = launch_status("mlp head (prep)");
   if (s != GE_OK) return s;
-  hipLaunchKernelGGL(mlp_head_kernel, dim3(nblocks), dim3(64), 0, st, H, (int)B, (int)D, (const half_t *)WT,
+  hipLaunchKernelGGL(mlp_head_kernel, dim3(nblocks), dim3(256), 0, st, H, (int)B, (int)D, (const half_t *)WT,
                      (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part);
   s = launch_status("mlp head");
   if (s != GE_OK) return s;
