@@ -27,8 +27,9 @@
 //    and the lane's own four G values gives lane l the four values
 //    dH[row l%16][h0 + 4(l/16) .. +3], masked by H of the same elements.
 //  * partial sums per block (in a fixed order): column sums of the rounded G
-//    and the sum of the row losses; the final kernel adds them in a fixed
-//    tree over the blocks.
+//    and the sum of the row losses, and column sums of the stored dH (the
+//    bias gradient of the layer below); final kernels add them over the
+//    blocks in a fixed order.
 #include "common.h"
 
 namespace ge {
@@ -44,6 +45,17 @@ typedef uint32_t hu32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(half_t, (uint16_t)bits16);
+}
+
+// Sum over each row of 16 lanes, valid in the row's lane 15: an inclusive
+// scan by DPP row shifts (1, 2, 4, 8; lanes shifted in from outside the row
+// read zero), VALU only and in a fixed order.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, true));
+  return v;
 }
 
 }  // namespace
@@ -65,7 +77,7 @@ __global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict_
                                                       int C, const int32_t *__restrict__ labels, float gscale,
                                                       float *__restrict__ Z, half_t *__restrict__ G,
                                                       float *__restrict__ row_loss, half_t *__restrict__ dH,
-                                                      float *__restrict__ part) {
+                                                      float *__restrict__ part, float *__restrict__ dpart) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   __shared__ f32x4 red[4][64];
@@ -251,14 +263,22 @@ __global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict_
           const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x16f16(w0[bf][u], gy, z0, 0, 0, 0);
           const f32x4 d1 = __builtin_amdgcn_mfma_f32_16x16x16f16(w1[bf][u], gy, z0, 0, 0, 0);
           const uint32_t bits = (mb[c >> 2] >> (8 * (c & 3))) & 0xffu;
-          if (rok) {
-            f16x8 o;
+          f16x8 o;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              o[t] = (half_t)(((bits >> t) & 1u) ? d0[t] : 0.f);
-              o[4 + t] = (half_t)(((bits >> (4 + t)) & 1u) ? d1[t] : 0.f);
-            }
-            *(f16x8 *)(drow + 32 * c) = o;
+          for (int t = 0; t < 4; ++t) {
+            o[t] = (half_t)(((bits >> t) & 1u) ? d0[t] : 0.f);
+            o[4 + t] = (half_t)(((bits >> (4 + t)) & 1u) ? d1[t] : 0.f);
+          }
+          if (rok) *(f16x8 *)(drow + 32 * c) = o;
+          // column sums of the stored dH over the block's 16 rows (the bias
+          // gradient of the layer below), a fixed butterfly over the rows
+          float cs[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) cs[t] = row16_sum(rok ? (float)o[t] : 0.f);
+          if (r16 == 15) {
+            float *dp = dpart + (int64_t)blockIdx.x * D + 32 * (cbase + c) + 8 * q;
+            *(f32x4 *)dp = f32x4{cs[0], cs[1], cs[2], cs[3]};
+            *(f32x4 *)(dp + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]};
           }
         }
       }
@@ -306,31 +326,36 @@ bool head_supported(int64_t B, int64_t D, int64_t C) {
   return B >= 1 && C >= 1 && C <= 16 && D >= 128 && D <= HEAD_DMAX && D % 128 == 0;
 }
 
-// partials, then the two layouts of W (256-byte aligned)
+// loss / class-column partials, the two layouts of W, then the per-block
+// column sums of dH (each region 256-byte aligned)
 int64_t head_ws_bytes(int64_t B, int64_t D) {
-  const int64_t p = (((B + HEAD_ROWS - 1) / HEAD_ROWS) * HEAD_PART * 4 + 255) / 256 * 256;
-  return p + 2 * D * 16 * 2;
+  const int64_t nb = (B + HEAD_ROWS - 1) / HEAD_ROWS;
+  const int64_t p = (nb * HEAD_PART * 4 + 255) / 256 * 256;
+  return p + 2 * D * 16 * 2 + nb * D * 4;
 }
 
 int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const float *bias, int64_t C,
                 const int32_t *labels, float gscale, float alpha, float *Z, half_t *G, float *row_loss,
-                half_t *dH, float *db, float *loss, void *ws, hipStream_t st) {
+                half_t *dH, float *db, float *db_below, float *loss, void *ws, hipStream_t st) {
   const int nblocks = (int)((B + HEAD_ROWS - 1) / HEAD_ROWS);
   float *part = (float *)ws;
   const int64_t p = ((int64_t)nblocks * HEAD_PART * 4 + 255) / 256 * 256;
   half_t *WT = (half_t *)((char *)ws + p);
   half_t *WP = WT + D * 16;
+  float *dpart = (float *)(WP + D * 16);
   hipLaunchKernelGGL(mlp_head_prep_kernel, dim3((unsigned)((D * 16 + 255) / 256)), dim3(256), 0, st, W, (int)D,
                      (int)C, WT, WP);
   int s = launch_status("mlp head (prep)");
   if (s != GE_OK) return s;
   hipLaunchKernelGGL(mlp_head_kernel, dim3(nblocks), dim3(256), 0, st, H, (int)B, (int)D, (const half_t *)WT,
-                     (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part);
+                     (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part, dpart);
   s = launch_status("mlp head");
   if (s != GE_OK) return s;
   hipLaunchKernelGGL(mlp_head_final_kernel, dim3(1), dim3(HEAD_PART * 32), 0, st, (const float *)part, nblocks,
                      (int)B, (int)C, alpha, db, loss);
-  return launch_status("mlp head (final)");
+  s = launch_status("mlp head (final)");
+  if (s != GE_OK) return s;
+  return colsum_partials_launch(dpart, nblocks, D, alpha, db_below, st);
 }
 
 }  // namespace ge

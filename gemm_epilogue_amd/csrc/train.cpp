@@ -214,7 +214,7 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
     // gradient dH_{L-1} (into the first ping-pong buffer) in one pass
     RUN(head_launch((const half_t *)hptr(nl - 1), B, d[nl - 1], (const half_t *)wptr(nl), buf->params + b_off[nl],
                     d[nl], labels, gscale, alpha, Z, (half_t *)G, row_loss, (half_t *)(ws + L.dh_off[0]),
-                    buf->grads + b_off[nl], loss_out, ws + L.head_off, s));
+                    buf->grads + b_off[nl], buf->grads + b_off[nl - 1], loss_out, ws + L.head_off, s));
   } else {
     RUN(xent_launch(Z, B, d[nl], d[nl], labels, gscale, loss_out, row_loss, G, d[nl], st, nullptr, s));
   }
@@ -229,7 +229,9 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
     a.workspace_bytes = L.gemm_ws;
     RUN(gemm_launch(a, s));
     const bool fused = L.head && l == nl;  // db and dH of this layer came from the head
-    if (!fused) RUN(colsum_launch(Gl, B, d[l], d[l], st, alpha, buf->grads + b_off[l], cws, L.cs_ws, s));
+    // the head also summed the columns of dH_{L-1}, the bias gradient of layer L-1
+    if (!(L.head && l >= nl - 1))
+      RUN(colsum_launch(Gl, B, d[l], d[l], st, alpha, buf->grads + b_off[l], cws, L.cs_ws, s));
     if (fused) {
       Gl = ws + L.dh_off[ping];
       ping ^= 1;
