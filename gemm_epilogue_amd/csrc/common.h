@@ -111,7 +111,6 @@ int64_t head_ws_bytes(int64_t B, int64_t D);
 int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const float *bias, int64_t C,
                 const int32_t *labels, float gscale, float alpha, float *Z, half_t *G, float *row_loss,
                 half_t *dH, float *db, float *db_below, float *loss, void *ws, hipStream_t st);
-int colsum_partials_launch(const float *part, int64_t splits, int64_t N, float alpha, float *out, hipStream_t st);
 int xent_launch(const float *logits, int64_t B, int64_t C, int64_t ld, const int32_t *labels,
                 float grad_scale, float *loss_mean, float *row_loss, void *dl, int64_t ld_d,
                 int d_type, int32_t *argmax, hipStream_t s);

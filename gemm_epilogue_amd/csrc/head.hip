@@ -296,29 +296,59 @@ __global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict_
   }
 }
 
-// Block partials -> bias gradient (alpha * column sums) and mean loss.  Each
-// of the 17 sums has 32 threads: thread j adds blocks j, j+32, ... in order,
-// then a fixed butterfly over the 32 threads.
+// Block partials -> bias gradient (alpha * column sums) and mean loss, and
+// the bias gradient of the layer below from the per-block column sums of dH.
+// Block 0: each of the 17 class sums has 32 threads; thread j adds blocks j,
+// j+32, ... in order, then a fixed butterfly over the 32 threads.  Blocks
+// 1..: 64 columns each; wave w adds partial rows w, w+8, ..., then the eight
+// wave sums are added in wave order.
 __global__ __launch_bounds__(HEAD_PART * 32) void mlp_head_final_kernel(const float *__restrict__ part,
                                                                          int nblocks, int B, int C, float alpha,
                                                                          float *__restrict__ db,
-                                                                         float *__restrict__ loss) {
-  const int col = threadIdx.x >> 5, j = threadIdx.x & 31;
-  float s = 0.f;
-  int b = j;
-  for (; b + 32 * 7 < nblocks; b += 32 * 8) {
-    float v[8];
+                                                                         float *__restrict__ loss,
+                                                                         const float *__restrict__ dpart, int D,
+                                                                         float *__restrict__ db_below) {
+  if (blockIdx.x == 0) {
+    const int col = threadIdx.x >> 5, j = threadIdx.x & 31;
+    float s = 0.f;
+    int b = j;
+    for (; b + 32 * 7 < nblocks; b += 32 * 8) {
+      float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(b + 32 * u) * HEAD_PART + col];
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(b + 32 * u) * HEAD_PART + col];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < nblocks; b += 32) s += part[(int64_t)b * HEAD_PART + col];
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (j == 0) {
+      if (col < C) db[col] = alpha * s;
+      if (col == 16) loss[0] = B > 0 ? s / (float)B : 0.f;
+    }
+    return;
   }
-  for (; b < nblocks; b += 32) s += part[(int64_t)b * HEAD_PART + col];
+  __shared__ float red[7][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;  // wave 8 (half a wave) idles
+  const int n = (blockIdx.x - 1) * 64 + lane;
+  float s = 0.f;
+  if (wave < 8 && n < D) {
+    int k = wave;
+    for (; k + 8 * 7 < nblocks; k += 8 * 8) {
+      float v[8];
 #pragma unroll
-  for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (j == 0) {
-    if (col < C) db[col] = alpha * s;
-    if (col == 16) loss[0] = B > 0 ? s / (float)B : 0.f;
+      for (int u = 0; u < 8; ++u) v[u] = dpart[(int64_t)(k + 8 * u) * D + n];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < nblocks; k += 8) s += dpart[(int64_t)k * D + n];
+  }
+  if (wave > 0 && wave < 8) red[wave - 1][lane] = s;
+  __syncthreads();
+  if (wave == 0 && n < D) {
+#pragma unroll
+    for (int w = 0; w < 7; ++w) s += red[w][lane];
+    db_below[n] = alpha * s;
   }
 }
 
@@ -351,11 +381,10 @@ int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const fl
                      (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part, dpart);
   s = launch_status("mlp head");
   if (s != GE_OK) return s;
-  hipLaunchKernelGGL(mlp_head_final_kernel, dim3(1), dim3(HEAD_PART * 32), 0, st, (const float *)part, nblocks,
-                     (int)B, (int)C, alpha, db, loss);
-  s = launch_status("mlp head (final)");
-  if (s != GE_OK) return s;
-  return colsum_partials_launch(dpart, nblocks, D, alpha, db_below, st);
+  hipLaunchKernelGGL(mlp_head_final_kernel, dim3((unsigned)(1 + (D + 63) / 64)), dim3(HEAD_PART * 32), 0, st,
+                     (const float *)part, nblocks, (int)B, (int)C, alpha, db, loss, (const float *)dpart, (int)D,
+                     db_below);
+  return launch_status("mlp head (final)");
 }
 
 }  // namespace ge

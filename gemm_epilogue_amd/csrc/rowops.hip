@@ -144,15 +144,6 @@ void colsum_partial_any(int xt, dim3 grid, hipStream_t st, const void *X, int M,
 }
 }  // namespace
 
-// out[n] = alpha * sum over k of part[k][n], in a fixed order (partials that
-// another kernel wrote, e.g. per-block column sums of a GEMM-like output)
-int colsum_partials_launch(const float *part, int64_t splits, int64_t N, float alpha, float *out, hipStream_t st) {
-  if (N == 0) return GE_OK;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, part, (int)splits,
-                     (int)N, alpha, out);
-  return launch_status("colsum (partials)");
-}
-
 int64_t colsum_ws_bytes(int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return 0;
   const int s = colsum_splits(M, N);
