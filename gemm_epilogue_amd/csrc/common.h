@@ -100,7 +100,13 @@ inline bool vec_aligned(const void *p, int64_t ld, int esize, int bytes) {
 }
 
 // internal launchers (validated arguments)
-int gemm_launch(const ge_gemm_args &a, hipStream_t s);
+// colpart (optional, 16-byte aligned): per-tile-row FP32 column sums of the
+// stored C, [gemm_colsum_rows(a) x N]; allowed when gemm_colsum_rows(a) > 0
+int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart = nullptr);
+int64_t gemm_colsum_rows(const ge_gemm_args &a);
+int64_t gemm_colsum_bytes(int ab_type, int64_t M, int64_t N, int64_t K);
+// out[n] = alpha * sum over r < rows of part[r][n], rows added in order
+int colsum_rows_launch(const float *part, int64_t rows, int64_t N, float alpha, float *out, hipStream_t st);
 int64_t gemm_ws_bytes(int layout, int ab_type, int64_t M, int64_t N, int64_t K, int split_k);
 int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int x_type, float alpha,
                   float *out, void *ws, int64_t ws_bytes, hipStream_t s);

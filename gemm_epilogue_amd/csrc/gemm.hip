@@ -171,9 +171,42 @@ int64_t gemm_ws_bytes(int layout, int ab_type, int64_t M, int64_t N, int64_t K, 
   return (int64_t)pl.splits * M * N * 4;
 }
 
-int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
+namespace {
+// the epilogue's 4-wide access checks (as store_tile's fast path reads them)
+int al4(const void *ptr, int64_t ld, int t) {
+  return ptr ? (int)vec_aligned(ptr, ld, dtype_size(t), 4 * dtype_size(t)) : 0;
+}
+// every tile of the plan takes the fast epilogue, K is not split and the
+// tile's kernel carries the column sums (all but the 256x256 tiles), so the
+// epilogue can also write per-tile-row column sums of C
+bool colsum_fusable(const Plan &pl, const ge_gemm_args &a) {
+  const bool bwd = a.act == GE_ACT_RELU_MASK_BWD || a.act == GE_ACT_LRELU_SQ_BWD;
+  return pl.splits == 1 && pl.bn < 256 && a.M % pl.bm == 0 && a.N % pl.bn == 0 && al4(a.C, a.ldc, a.c_type) &&
+         (!a.aux || al4(a.aux, a.ld_aux, a.aux_type)) && (!a.residual || al4(a.residual, a.ld_res, a.res_type)) &&
+         (!a.pre || al4(a.pre, a.ld_pre, a.pre_type)) && (!a.bias || ((uintptr_t)a.bias % 16) == 0) &&
+         !(bwd && a.residual);
+}
+}  // namespace
+
+int64_t gemm_colsum_rows(const ge_gemm_args &a) {
+  if (a.M <= 0 || a.N <= 0) return 0;
+  Plan pl = make_plan(a.ab_type, a.M, a.N, a.K, a.split_k);
+  return colsum_fusable(pl, a) ? pl.tiles_m : 0;
+}
+
+int64_t gemm_colsum_bytes(int ab_type, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 0;
+  Plan pl = make_plan(ab_type, M, N, K, 0);
+  return pl.splits == 1 && pl.bn < 256 ? (int64_t)pl.tiles_m * N * 4 : 0;
+}
+
+int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart) {
   if (a.M == 0 || a.N == 0) return GE_OK;
   Plan pl = make_plan(a.ab_type, a.M, a.N, a.K, a.split_k);
+  if (colpart != nullptr && (!colsum_fusable(pl, a) || ((uintptr_t)colpart % 16) != 0)) {
+    set_error("gemm_bias_act: column sums in the epilogue need unsplit, whole, aligned tiles");
+    return GE_E_INVALID;
+  }
   GemmParams gp;
   const int es = dtype_size(a.ab_type);
   gp.A = a.A;
@@ -227,9 +260,7 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s) {
   e.pre_type = a.pre_type;
   e.M = (int)a.M;
   e.N = (int)a.N;
-  auto al4 = [](const void *ptr, int64_t ld, int t) {
-    return ptr ? (int)vec_aligned(ptr, ld, dtype_size(t), 4 * dtype_size(t)) : 0;
-  };
+  e.colpart = colpart;
   e.aux_vec = al4(a.aux, a.ld_aux, a.aux_type);
   e.res_vec = al4(a.residual, a.ld_res, a.res_type);
   e.c_vec = al4(a.C, a.ldc, a.c_type);

@@ -52,6 +52,10 @@ struct EpiParams {
   int pre_type;
   int M, N;
   int aux_vec, res_vec, c_vec, pre_vec, bias_vec;
+  // optional: per-tile-row column sums of the stored C ([tiles_m x N] FP32),
+  // for the bias gradient of a layer whose dZ this GEMM writes; the host sets
+  // it only when every tile takes the fast epilogue and K is not split
+  float *colpart;
 };
 
 struct GemmParams {
@@ -200,11 +204,18 @@ template <int CS> __device__ __forceinline__ void store_c4(void *C, int64_t i, i
   }
 }
 
+// the value a store of v in the output type leaves in memory
+template <int CS> __device__ __forceinline__ float stored_value(float v, int ct) {
+  if constexpr (CS == 4) return v;
+  else return ct == GE_F16 ? (float)(half_t)v : (float)(bf16_t)v;
+}
+
 // Rows m_base + r0 + q*RS (q < RPT) of the staged tile, columns n..n+3,
-// in batches of EU rows.
-template <int CS, int XS, int RPT, int EU, int RS, int CSTRIDE>
+// in batches of EU rows; with CSUM and e.colpart, csum gathers the stored
+// values.
+template <int CS, int XS, int RPT, int EU, int RS, int CSTRIDE, bool CSUM>
 __device__ __forceinline__ void epi_rows_fast(const EpiParams &e, const float *cs, int m_base, int r0, int cg,
-                                              int n, const float b[4]) {
+                                              int n, const float b[4], float (&csum)[4]) {
   const bool bwd = e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD;
   const char *xp = (const char *)(bwd ? e.aux : e.res);
   const int64_t ldx = bwd ? e.ld_aux : e.ld_res;
@@ -257,6 +268,12 @@ __device__ __forceinline__ void epi_rows_fast(const EpiParams &e, const float *c
         for (int j = 0; j < 4; ++j) v[j] += x[j];
       }
       store_c4<CS>(e.C, m * e.ldc + n, e.c_type, v);
+      if constexpr (CSUM) {
+        if (e.colpart) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) csum[j] += stored_value<CS>(v[j], e.c_type);
+        }
+      }
     }
   }
 }
@@ -598,8 +615,10 @@ __device__ __forceinline__ void block_work(const GemmParams &p, int BM, int BN, 
 // ---- epilogue of one BM x BN tile ---------------------------------------------------
 // acc[i][j] holds the 16x16 block (wm0 + 16i, wn0 + 16j) of the tile, lane l
 // owning row l % 16, columns 4(l / 16) .. +3.  The tile is staged through LDS
-// in NPASS passes of BM / NPASS rows.
-template <int BM, int BN, int NT, int FM, int FN, int NPASS, int EUQ = 0>
+// in NPASS passes of BM / NPASS rows.  CSUM: the kernel has the registers
+// to also gather column sums for e.colpart (the 256x256 tiles do not: the
+// four accumulators spill there).
+template <int BM, int BN, int NT, int FM, int FN, int NPASS, int EUQ = 0, bool CSUM = false>
 __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x4 (&acc)[FM][FN], int tid, int wm0,
                                            int wn0, int bm0, int bn0, int split) {
   const int lane = tid & 63;
@@ -630,6 +649,7 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x
   const bool bwd = e.act == GE_ACT_RELU_MASK_BWD || e.act == GE_ACT_LRELU_SQ_BWD;
   const void *xin = bwd ? e.aux : e.res;
   const int xin_type = bwd ? e.aux_type : e.res_type;
+  float csum[4] = {0.f, 0.f, 0.f, 0.f};
   for (int pass = 0; pass < NPASS; ++pass) {
     if (wm0 / RP == pass) {
 #pragma unroll
@@ -663,13 +683,13 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x
     } else if (fast && !(bwd && e.res)) {
       const int xs = xin == nullptr ? 0 : (xin_type == GE_F32 ? 4 : 2);
       if (e.c_type == GE_F32) {
-        if (xs == 0) epi_rows_fast<4, 0, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else if (xs == 2) epi_rows_fast<4, 2, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else epi_rows_fast<4, 4, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+        if (xs == 0) epi_rows_fast<4, 0, RPT, EU, RS, CSTRIDE, CSUM>(e, cs, m_base, r0, cg, n, bias, csum);
+        else if (xs == 2) epi_rows_fast<4, 2, RPT, EU, RS, CSTRIDE, CSUM>(e, cs, m_base, r0, cg, n, bias, csum);
+        else epi_rows_fast<4, 4, RPT, EU, RS, CSTRIDE, CSUM>(e, cs, m_base, r0, cg, n, bias, csum);
       } else {
-        if (xs == 0) epi_rows_fast<2, 0, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else if (xs == 2) epi_rows_fast<2, 2, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
-        else epi_rows_fast<2, 4, RPT, EU, RS, CSTRIDE>(e, cs, m_base, r0, cg, n, bias);
+        if (xs == 0) epi_rows_fast<2, 0, RPT, EU, RS, CSTRIDE, CSUM>(e, cs, m_base, r0, cg, n, bias, csum);
+        else if (xs == 2) epi_rows_fast<2, 2, RPT, EU, RS, CSTRIDE, CSUM>(e, cs, m_base, r0, cg, n, bias, csum);
+        else epi_rows_fast<2, 4, RPT, EU, RS, CSTRIDE, CSUM>(e, cs, m_base, r0, cg, n, bias, csum);
       }
     } else {
       // edge tiles and unaligned operands: checked element access
@@ -688,6 +708,19 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x
       }
     }
     __syncthreads();
+  }
+  if (CSUM && e.colpart != nullptr) {
+    // column sums of the tile: thread (cg, r0) holds rows r0, r0 + RS, ... of
+    // every pass; the RS row groups are added in order through LDS
+    float *red = (float *)smem;
+    *(f32x4 *)(red + r0 * BN + cg * 4) = f32x4{csum[0], csum[1], csum[2], csum[3]};
+    __syncthreads();
+    if (tid < CG) {
+      f32x4 t = *(const f32x4 *)(red + tid * 4);
+#pragma unroll
+      for (int r = 1; r < RS; ++r) t += *(const f32x4 *)(red + r * BN + tid * 4);
+      *(f32x4 *)(e.colpart + (int64_t)(bm0 / BM) * p.N + bn0 + tid * 4) = t;
+    }
   }
 }
 
@@ -877,7 +910,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN >= 8 ? 1 : 2)) void gemm
     }
   }
 
-  store_tile<BM, BN, NT, FM, FN, NPASS>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
+  store_tile<BM, BN, NT, FM, FN, NPASS, 0, (BM < 256)>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
 }
 
 // ---- 256 x BN tile on four waves (BN = 256 or 128) ------------------------------------
@@ -1084,7 +1117,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
     }
     __syncthreads();
   }
-  store_tile<BM, BN, NT, FM, FN, NPASS, 4>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
+  store_tile<BM, BN, NT, FM, FN, NPASS, 4, (BN < 256)>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
 }
 
 // ---- launch plan and per-type launchers ---------------------------------------

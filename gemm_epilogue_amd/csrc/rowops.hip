@@ -144,6 +144,13 @@ void colsum_partial_any(int xt, dim3 grid, hipStream_t st, const void *X, int M,
 }
 }  // namespace
 
+int colsum_rows_launch(const float *part, int64_t rows, int64_t N, float alpha, float *out, hipStream_t st) {
+  if (N == 0) return GE_OK;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, part, (int)rows,
+                     (int)N, alpha, out);
+  return launch_status("colsum (rows)");
+}
+
 int64_t colsum_ws_bytes(int64_t M, int64_t N) {
   if (M <= 0 || N <= 0) return 0;
   const int s = colsum_splits(M, N);

@@ -73,6 +73,8 @@ MlpLayout layout_of(const ge_mlp_desc *d, int64_t B) {
     gws = std::max(gws, gemm_ws_bytes(GE_TN, t, din, dout, B, 0));
     if (l > 1) gws = std::max(gws, gemm_ws_bytes(GE_NT, t, B, din, dout, 0));
     cws = std::max(cws, colsum_ws_bytes(B, dout));
+    // or the column partials the masked dgrad GEMM's epilogue writes
+    if (l > 1) cws = std::max(cws, gemm_colsum_bytes(t, B, din, dout));
   }
   L.gemm_ws_off = off;
   L.gemm_ws = gws;
@@ -221,6 +223,7 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   // backward
   const void *Gl = G;
   int ping = 0;
+  int64_t gl_rows = 0;  // > 0: the GEMM that wrote Gl left its column partials in cws
   for (int l = nl; l >= 1; --l) {
     ge_gemm_args a = gemm_args(GE_TN, st, d[l - 1], d[l], B, hptr(l - 1), d[l - 1], Gl, d[l],
                                buf->grads + w_off[l], d[l], GE_F32);
@@ -230,8 +233,13 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
     RUN(gemm_launch(a, s));
     const bool fused = L.head && l == nl;  // db and dH of this layer came from the head
     // the head also summed the columns of dH_{L-1}, the bias gradient of layer L-1
-    if (!(L.head && l >= nl - 1))
-      RUN(colsum_launch(Gl, B, d[l], d[l], st, alpha, buf->grads + b_off[l], cws, L.cs_ws, s));
+    if (!(L.head && l >= nl - 1)) {
+      if (gl_rows > 0)
+        RUN(colsum_rows_launch((const float *)cws, gl_rows, d[l], alpha, buf->grads + b_off[l], s));
+      else
+        RUN(colsum_launch(Gl, B, d[l], d[l], st, alpha, buf->grads + b_off[l], cws, L.cs_ws, s));
+    }
+    gl_rows = 0;
     if (fused) {
       Gl = ws + L.dh_off[ping];
       ping ^= 1;
@@ -244,7 +252,13 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
       b.aux_type = st;
       b.workspace = gws;
       b.workspace_bytes = L.gemm_ws;
-      RUN(gemm_launch(b, s));
+      // the bias gradient of layer l-1 is the column sum of this dZ: let the
+      // epilogue sum each tile's columns when the whole output takes its
+      // fast path, leaving a few partial rows for the next step
+      const int64_t rows = gemm_colsum_rows(b);
+      const bool part = rows > 0 && cws != nullptr && rows * d[l - 1] * 4 <= L.cs_ws;
+      RUN(gemm_launch(b, s, part ? (float *)cws : nullptr));
+      gl_rows = part ? rows : 0;
       Gl = dH;
       ping ^= 1;
     }
