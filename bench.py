@@ -34,7 +34,7 @@ PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16/BF16 MFMA
 # by the counters' reading for a plain copy of known size (--copy-calibration),
 # as listed in profiles/mlp784-2048-2048-10_fp16_b4096_hbm_bytes.md.  Taken on
 # the current kernel; to be re-measured whenever the kernel changes.
-NN_TRAFFIC_BYTES = 101.19e6
+NN_TRAFFIC_BYTES = 101.24e6
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 DIMS = [784, 2048, 2048, 10]
 BATCH, LR, MU, N_BATCHES = 4096, 0.05, 0.9, 50
