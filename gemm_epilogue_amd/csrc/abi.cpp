@@ -144,7 +144,8 @@ int sgd_momentum(float *w, const float *g, float *v, float lr, float momentum, i
   if (n == 0) return GE_OK;
   CHECK(w != nullptr && g != nullptr && v != nullptr, "sgd_momentum: w, g or v is NULL");
   if (w_lowp) CHECK(lowp_type == GE_F16 || lowp_type == GE_BF16, "sgd_momentum: lowp_type must be F16 or BF16");
-  return sgd_launch(w, g, v, lr, momentum, n, w_lowp, lowp_type, (hipStream_t)stream);
+  // without a gradient segment the update only reads g
+  return sgd_launch(w, const_cast<float *>(g), v, lr, momentum, n, w_lowp, lowp_type, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -122,7 +122,11 @@ int xent_launch(const float *logits, int64_t B, int64_t C, int64_t ld, const int
                 int d_type, int32_t *argmax, hipStream_t s);
 int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t s);
 int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D);
-int sgd_launch(float *w, const float *g, float *v, float lr, float mu, int64_t n, void *wl,
-               int lt, hipStream_t s);
+// seg_part (optional): g[seg_g0 .. seg_g0 + seg_len) is first set to
+// seg_alpha times the sum of seg_rows partial rows [seg_rows x seg_len] (g is
+// written only then)
+int sgd_launch(float *w, float *g, float *v, float lr, float mu, int64_t n, void *wl, int lt, hipStream_t s,
+               const float *seg_part = nullptr, int64_t seg_g0 = 0, int64_t seg_len = 0, int seg_rows = 0,
+               float seg_alpha = 1.f);
 
 }  // namespace ge

@@ -224,6 +224,7 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   const void *Gl = G;
   int ping = 0;
   int64_t gl_rows = 0;  // > 0: the GEMM that wrote Gl left its column partials in cws
+  int seg_rows = 0;     // > 0: db1 still to be formed from cws by the update
   for (int l = nl; l >= 1; --l) {
     ge_gemm_args a = gemm_args(GE_TN, st, d[l - 1], d[l], B, hptr(l - 1), d[l - 1], Gl, d[l],
                                buf->grads + w_off[l], d[l], GE_F32);
@@ -234,7 +235,10 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
     const bool fused = L.head && l == nl;  // db and dH of this layer came from the head
     // the head also summed the columns of dH_{L-1}, the bias gradient of layer L-1
     if (!(L.head && l >= nl - 1)) {
-      if (gl_rows > 0)
+      if (gl_rows > 0 && l == 1) {
+        // no GEMM follows to reuse cws: the momentum update forms db1 itself
+        seg_rows = (int)gl_rows;
+      } else if (gl_rows > 0)
         RUN(colsum_rows_launch((const float *)cws, gl_rows, d[l], alpha, buf->grads + b_off[l], s));
       else
         RUN(colsum_launch(Gl, B, d[l], d[l], st, alpha, buf->grads + b_off[l], cws, L.cs_ws, s));
@@ -265,7 +269,7 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   }
   (void)es;
   return sgd_launch(buf->params, buf->grads, buf->velocity, lr, momentum, P, f16 ? buf->params_lowp : nullptr,
-                    GE_F16, s);
+                    GE_F16, s, seg_rows > 0 ? (const float *)cws : nullptr, b_off[1], d[1], seg_rows, alpha);
 }
 
 }  // extern "C"
