@@ -90,9 +90,15 @@ def mlp_step(params, vel, dims, X, labels, lr: float, momentum: float,
     bits are correct within the forward rounding error); the number of such
     adopted bits that differ is reported as ``mask_ties``.
 
-    ``given``: optional dict of the GPU's stored tensors -- "H" [H1, ...],
-    "Z", "G", "dH" [dH_1, ...] (dH_l is the masked gradient at H_l) -- each
-    stage then starts from the stored inputs it consumed (stage-wise check).
+    ``given``: optional dict of stored tensors -- "H" [H1, ...], "Z", "G",
+    "dH" [dH_1, ...] (dH_l is the masked gradient at H_l) -- each stage then
+    starts from the stored inputs it consumed (stage-wise check).  The given
+    tensors are inputs only: every returned tensor is the oracle's own value,
+    computed from the inputs of its stage.  So "H"[l] is layer l+1's output
+    computed from given H_l (X for the first layer), "Z" is computed from the
+    given last hidden layer, "argmax" from that own "Z", while "loss",
+    "row_loss" and "G" are the loss stage applied to the given "Z" and the
+    weight gradients use the given H and G / dH as their operands.
     """
     P = _plan(plan)
     given = given or {}
@@ -102,12 +108,15 @@ def mlp_step(params, vel, dims, X, labels, lr: float, momentum: float,
     L = len(layers)
     gH = given.get("H")
     Hs, pres, Z = mlp_forward(params, dims, X, plan, given_H=gH)
+    H_own = Hs[1:]
     if gH is not None:
+        # the backward stages consume the stored activations
         Hs = [Hs[0]] + [np.asarray(h, np.float64) for h in gH]
     grad_scale = 1.0 if P["unscaled"] else 1.0 / B
     alpha = 1.0 / B if P["unscaled"] else 1.0
     Zin = np.asarray(given["Z"], np.float64) if "Z" in given else Z
-    loss, row_loss, G, argmax = softmax_xent(Zin, labels, grad_scale, P["dz"])
+    loss, row_loss, G, _ = softmax_xent(Zin, labels, grad_scale, P["dz"])
+    argmax = np.asarray(Z).argmax(axis=1).astype(np.int32)
     grads = [None] * L
     dHs = [None] * L
     ties = 0
@@ -139,7 +148,7 @@ def mlp_step(params, vel, dims, X, labels, lr: float, momentum: float,
     else:
         wnew, vnew, wlow = sgd_momentum(params, gflat, vel, lr, momentum,
                                         "f16" if plan == "f16" else None)
-    return dict(loss=loss, row_loss=row_loss, Z=Z, G=G, argmax=argmax, H=Hs[1:],
+    return dict(loss=loss, row_loss=row_loss, Z=Z, G=G, argmax=argmax, H=H_own,
                 pre=pres, dH=dHs[:-1] if L > 1 else [], grads=gflat,
                 params=wnew, vel=vnew, params_lowp=wlow, mask_ties=ties)
 

@@ -29,6 +29,11 @@ STAGES = {"GI": ("GI", "f32"), "HS": ("hs", "f32"), "R": ("R", "f32"), "Z": ("Zg
           "N": ("N", "f32"), "HN": ("hn", "f16"), "RSTD": ("rstd", "f32"), "LOGITS": ("logits", "f32"),
           "G": ("G", "f16"), "DHN": ("dhn", "f32"), "DH_OUT": ("dh_out", "f32"), "DGH": ("dGH", "f16"),
           "DGI": ("dGI", "f16"), "DX": ("dX", "f32")}
+# stages whose values are formed from cancelling sums (GEMM outputs, the
+# recurrence mix (1-z) n + z h, tanh of GI_n + r GH_n, the RMSNorm input
+# gradient, the carried gate gradients); r, z (sigmoids), hn, rstd and the
+# softmax gradient are held to the plain rule
+NO_CANCEL = ("R", "Z", "HN", "RSTD", "G")
 GIVEN = {"HS": "hs", "R": "R", "Z": "Z", "N": "N", "GH": "GH", "RSTD": "rstd", "HN": "hn",
          "LOGITS": "logits", "G": "G", "DHN": "dhn", "DH_OUT": "dh_out", "DGH": "dGH", "DGI": "dGI",
          "DX": "dX"}
@@ -50,14 +55,14 @@ def _run_and_check(ge, V, H, B, T, lr, mu, params, what, steps=1):
         loss = host(tr.loss)[0]
         assert abs(loss - ref["loss"]) <= TOL_LOSS * abs(ref["loss"]), (what, loss, ref["loss"])
         for k, (rk, fmt) in STAGES.items():
-            assert_parity(got[k], ref[rk], TOL_LOWP, fmt, f"{what} {k}")
-        assert_parity(host(tr.grads), ref["grads"], TOL_LOWP, "f32", f"{what} grads")
-        assert_parity(host(tr.params), ref["params"], TOL_LOWP, "f32", f"{what} params")
+            assert_parity(got[k], ref[rk], TOL_LOWP, fmt, f"{what} {k}", cancel=k not in NO_CANCEL)
+        assert_parity(host(tr.grads), ref["grads"], TOL_LOWP, "f32", f"{what} grads", cancel=True)
+        assert_parity(host(tr.params), ref["params"], TOL_LOWP, "f32", f"{what} params", cancel=True)
         np.testing.assert_array_equal(host(tr.params_lowp), oracle.round_fmt(host(tr.params), "f16"))
         # end to end from the pre-step state (oracle's own intermediates): reported
         e2e = oracle.gru_step(w0, v0, tok, H, V, lr, mu, eps=1e-6, plan="f16")
         rl = abs(loss - e2e["loss"]) / e2e["loss"]
-        c = compare(host(tr.grads), e2e["grads"], TOL_LOWP, "f32")
+        c = compare(host(tr.grads), e2e["grads"], TOL_LOWP, "f32", cancel=True)
         print(f"{what} step {s}: end-to-end loss rel diff {rl:.2e}, grads cos {c['cos']:.8f}")
         assert rl < 1e-3 and c["cos"] > 0.9999
     return tr
@@ -100,6 +105,6 @@ def test_embedding_gather_and_grad(ge):
     g = ge.embedding_grad(torch.from_numpy(dX).float().cuda(), torch.from_numpy(vi).cuda(), V, 0.5)
     dE = np.zeros((V, H))
     np.add.at(dE, vi, dX)
-    assert_parity(host(g), oracle.round_fmt(0.5 * dE, "f32"), 1e-4, "f32", "dE")
+    assert_parity(host(g), oracle.round_fmt(0.5 * dE, "f32"), 1e-4, "f32", "dE", cancel=True)
     g2 = ge.embedding_grad(torch.from_numpy(dX).float().cuda(), torch.from_numpy(vi).cuda(), V, 0.5)
     assert torch.equal(g, g2)

@@ -1,6 +1,17 @@
 """GPU parity of mlp_train_step: the 784-256-10 FP32 epoch and the
-784-2048-2048-10 FP16 step, lock-step against the oracle (each step starts
-from the GPU's own pre-step parameters and velocity)."""
+784-2048-2048-10 FP16 step, lock-step against the oracle (each checked step
+starts from the GPU's own pre-step parameters and velocity).
+
+Two comparisons per checked step:
+
+* stage-wise: every stored tensor against the oracle's own value computed
+  from the stored inputs that stage consumed (the oracle's ``given=`` mode
+  only feeds inputs; everything it returns is its own);
+* end-to-end: the step's loss, argmax and update against the oracle's own
+  whole step from the same pre-step state, under the loss and argmax rules
+  (loss within 1e-5 relative on the FP32 path; argmax identical unless the
+  oracle's top-2 logit gap is below 1e-4).
+"""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +21,15 @@ import oracle
 from parity import TOL_F32, TOL_LOSS, TOL_LOWP, assert_parity, compare
 
 pytestmark = pytest.mark.gpu
+
+# Largest end-to-end relative loss difference accepted for FP16 storage:
+# there the oracle's own step rounds H1, H2 and dZ to FP16 from FP64 values
+# while the GPU rounds FP32 accumulations, so an element at a rounding
+# boundary lands one FP16 ulp (2^-11 relative) apart and the difference
+# propagates into the logits.  The bound is the largest difference observed
+# on the 784-2048-2048-10 steps times a margin; the stage-wise loss (the loss
+# kernel on its own stored input) is held to 1e-5.
+E2E_LOSS_F16 = 2e-4
 
 
 @pytest.fixture(scope="module")
@@ -23,11 +43,16 @@ def host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def _argmax_ok(Z_gpu, Z_ref):
+    srt = np.sort(Z_ref, axis=1)
+    gap = srt[:, -1] - srt[:, -2]
+    pred = Z_gpu.argmax(axis=1)
+    ref = Z_ref.argmax(axis=1)
+    return (pred == ref) | (gap < 1e-4), int(np.count_nonzero(pred != ref))
+
+
 def _check_step(tr, dims, X, y, lr, mu, plan, w0, v0, tie_abs, what):
-    """Stage-wise check: every stored tensor against the oracle applied to the
-    stored inputs that stage consumed (strict rule); then the oracle's own
-    end-to-end step, where one-ulp storage differences propagate (reported,
-    loosely bounded)."""
+    """Stage-wise check of every stored tensor, then the end-to-end rules."""
     B = X.shape[0]
     ws = tr.workspace_views(B)
     torch.cuda.synchronize()
@@ -38,35 +63,45 @@ def _check_step(tr, dims, X, y, lr, mu, plan, w0, v0, tie_abs, what):
     given = {"H": H_gpu, "Z": Z, "G": host(ws["G"]), "dH": [host(h) for h in ws["dH"]]}
     ref = oracle.mlp_step(w0, v0, dims, X, y, lr, mu, plan=plan, given=given)
     loss = host(tr.loss)[0]
+    # the loss stage on the logits it consumed
     assert abs(loss - ref["loss"]) <= TOL_LOSS * abs(ref["loss"]), (what, loss, ref["loss"])
+    # each layer's output against the oracle's layer applied to that layer's stored input
     for i, (hg, hr) in enumerate(zip(H_gpu, ref["H"])):
-        assert_parity(hg, hr, tol, fmt, f"{what} H{i + 1}")
-    assert_parity(Z, ref["Z"], tol, "f32", f"{what} Z")
+        assert_parity(hg, hr, tol, fmt, f"{what} H{i + 1}", cancel=True)
+    assert_parity(Z, ref["Z"], tol, "f32", f"{what} Z", cancel=True)
     assert_parity(given["G"], ref["G"], tol, fmt, f"{what} G")
     for i, (dg, dr) in enumerate(zip(given["dH"], ref["dH"])):
-        assert_parity(dg, dr, tol, fmt, f"{what} dH{i + 1}")
-    assert_parity(host(tr.grads), ref["grads"], tol, "f32", f"{what} grads")
-    assert_parity(host(tr.velocity), ref["vel"], tol, "f32", f"{what} velocity")
-    assert_parity(host(tr.params), ref["params"], tol, "f32", f"{what} params")
+        assert_parity(dg, dr, tol, fmt, f"{what} dH{i + 1}", cancel=True)
+    assert_parity(host(tr.grads), ref["grads"], tol, "f32", f"{what} grads", cancel=True)
+    assert_parity(host(tr.velocity), ref["vel"], tol, "f32", f"{what} velocity", cancel=True)
+    assert_parity(host(tr.params), ref["params"], tol, "f32", f"{what} params", cancel=True)
     if plan == "f16":
         np.testing.assert_array_equal(host(tr.params_lowp), oracle.round_fmt(host(tr.params), "f16"))
-    srt = np.sort(ref["Z"], axis=1)
-    gap = srt[:, -1] - srt[:, -2]
-    pred = Z.argmax(axis=1)
-    assert np.all((pred == ref["argmax"]) | (gap < 1e-4)), what
+    # argmax rule, stage-wise: the GPU's logits against the oracle's logits
+    # computed from the same stored last hidden layer
+    ok, nd = _argmax_ok(Z, ref["Z"])
+    assert np.all(ok), (what, nd)
     # end to end from the pre-step state, the oracle's own intermediates
     e2e = oracle.mlp_step(w0, v0, dims, X, y, lr, mu, plan=plan, mask_hint=H_gpu, tie_abs=tie_abs)
     rl = abs(loss - e2e["loss"]) / abs(e2e["loss"])
-    gc = compare(host(tr.grads), e2e["grads"], tol, "f32")
-    print(f"{what}: end-to-end loss rel diff {rl:.2e}, grads cos {gc['cos']:.9f}, "
-          f"mask ties adopted {e2e['mask_ties']}")
-    assert rl < 1e-3 and gc["cos"] > 0.99999, what
-    assert_parity(host(tr.params), e2e["params"], tol, "f32", f"{what} params end-to-end")
-    return ref
+    gc = compare(host(tr.grads), e2e["grads"], tol, "f32", cancel=True)
+    ok_e, nd_e = _argmax_ok(Z, e2e["Z"])
+    print(f"{what}: end-to-end loss rel diff {rl:.3e}, argmax differs in {nd_e} rows "
+          f"({int(np.count_nonzero(~ok_e))} outside the top-2 gap rule), grads cos {gc['cos']:.9f}, "
+          f"mask ties adopted {e2e['mask_ties']}", flush=True)
+    if plan == "f32":
+        assert rl <= TOL_LOSS, (what, rl)
+        assert np.all(ok_e), (what, nd_e)
+        assert_parity(host(tr.params), e2e["params"], tol, "f32", f"{what} params end-to-end", cancel=True)
+    else:
+        assert rl <= E2E_LOSS_F16, (what, rl)
+        assert gc["cos"] > 0.99999, what
+    return ref, e2e, rl
 
 
 def test_cfg0_epoch_lockstep(ge, pins):
-    """One epoch of the 784-256-10 FP32 net: 46 batches of 128 and one of 112."""
+    """One epoch of the 784-256-10 FP32 net: 46 batches of 128 and one of 112,
+    every step checked stage-wise and end-to-end (loss within 1e-5)."""
     dims = datagen.mlp_dims_cfg0()
     lr, mu, bs = pins["lr"], pins["momentum"], pins["batch"]
     Xall, yall = datagen.template_images(6000, 100, fmt="f32")
@@ -74,19 +109,22 @@ def test_cfg0_epoch_lockstep(ge, pins):
     tr = ge.MLPTrainer(dims, bs, torch.float32, params=torch.from_numpy(p0).float().cuda())
     tX = torch.from_numpy(Xall).float().cuda()
     ty = torch.from_numpy(yall).cuda()
-    n_steps = 0
+    n_steps, worst = 0, 0.0
     for s in range(0, 6000, bs):
         e = min(6000, s + bs)
         w0, v0 = host(tr.params), host(tr.velocity)
         tr.step(tX[s:e], ty[s:e], lr, mu)
-        _check_step(tr, dims, Xall[s:e], yall[s:e], lr, mu, "f32", w0, v0, 1e-6, f"step {n_steps}")
+        _, _, rl = _check_step(tr, dims, Xall[s:e], yall[s:e], lr, mu, "f32", w0, v0, 1e-6, f"step {n_steps}")
+        worst = max(worst, rl)
         n_steps += 1
     assert n_steps == 47
+    print(f"784-256-10 epoch: worst end-to-end loss rel diff over 47 steps {worst:.3e}")
 
 
-def test_cfg0_free_running_loss(ge, pins):
-    """Independent trajectories (GPU vs oracle, both from the initial weights):
-    the loss curve is reported; errors compound, so only drift is bounded."""
+def test_cfg0_free_running(ge, pins):
+    """Independent trajectories (GPU vs oracle, both from the initial weights)
+    over the epoch: the loss curve and the final argmax are reported under the
+    loss and argmax rules."""
     dims = datagen.mlp_dims_cfg0()
     lr, mu, bs = pins["lr"], pins["momentum"], pins["batch"]
     Xall, yall = datagen.template_images(6000, 100, fmt="f32")
@@ -95,15 +133,23 @@ def test_cfg0_free_running_loss(ge, pins):
     tX = torch.from_numpy(Xall).float().cuda()
     ty = torch.from_numpy(yall).cuda()
     w, v = p0.copy(), np.zeros_like(p0)
-    worst = 0.0
+    rels = []
     for s in range(0, 6000, bs):
         e = min(6000, s + bs)
         tr.step(tX[s:e], ty[s:e], lr, mu)
         ref = oracle.mlp_step(w, v, dims, Xall[s:e], yall[s:e], lr, mu, plan="f32")
         w, v = ref["params"], ref["vel"]
-        worst = max(worst, abs(host(tr.loss)[0] - ref["loss"]) / ref["loss"])
-    print(f"free-running worst relative loss drift over the epoch: {worst:.3e}")
-    assert worst < 1e-2
+        rels.append(abs(host(tr.loss)[0] - ref["loss"]) / ref["loss"])
+    # final argmax over the whole epoch's images with the two final weight sets
+    tr.step(tX[:bs], ty[:bs], 0.0, 0.0)     # lr 0: logits of the final weights, no update
+    torch.cuda.synchronize()
+    Zg = host(tr.workspace_views(bs)["Z"])
+    Zr = oracle.mlp_forward(w, dims, Xall[:bs], "f32")[2]
+    ok, nd = _argmax_ok(Zg, Zr)
+    print(f"free-running: loss rel diff first {rels[0]:.3e}, last {rels[-1]:.3e}, "
+          f"worst {max(rels):.3e}; final argmax differs in {nd}/{bs} rows")
+    assert max(rels) <= TOL_LOSS
+    assert np.all(ok)
 
 
 def test_overfit_32(ge, pins):
@@ -118,18 +164,73 @@ def test_overfit_32(ge, pins):
     assert host(tr.loss)[0] < pins["overfit_loss_below"]
 
 
-def test_cfg2_step_lockstep(ge):
-    """784-2048-2048-10, FP16 storage, batch 4096, lr 0.05, momentum 0.9: two steps."""
+CFG2_CHECKED = (1, 2, 10, 25, 50)   # 1-based steps of the 50-step run checked lock-step
+
+
+@pytest.mark.timeout(900)
+def test_cfg2_run_lockstep(ge):
+    """784-2048-2048-10, FP16 storage, batch 4096, lr 0.05, momentum 0.9: the
+    50-step run, lock-step checks at steps 1, 2, 10, 25 and 50."""
     dims = datagen.mlp_dims_cfg2()
     B, lr, mu = 4096, 0.05, 0.9
     p0 = datagen.he_uniform_flat(dims)
     tr = ge.MLPTrainer(dims, B, torch.float16, params=torch.from_numpy(p0).float().cuda())
-    for step in range(2):
-        X, y = datagen.template_images(B, 200, fmt="f16", batch=step)
-        w0, v0 = host(tr.params), host(tr.velocity)
-        print(f"cfg2 step {step}", flush=True)
+    rls = []
+    for step in range(1, 51):
+        X, y = datagen.template_images(B, 200, fmt="f16", batch=step - 1)
+        check = step in CFG2_CHECKED
+        if check:
+            w0, v0 = host(tr.params), host(tr.velocity)
         tr.step(torch.from_numpy(X).half().cuda(), torch.from_numpy(y).cuda(), lr, mu)
-        _check_step(tr, dims, X, y, lr, mu, "f16", w0, v0, 1e-5, f"cfg2 step {step}")
+        if check:
+            print(f"784-2048-2048-10 step {step}: checking", flush=True)
+            rls.append(_check_step(tr, dims, X, y, lr, mu, "f16", w0, v0, 1e-5, f"cfg2 step {step}")[2])
+    print(f"784-2048-2048-10 lock-step: end-to-end loss rel diffs {['%.2e' % r for r in rls]}")
+
+
+@pytest.mark.timeout(900)
+def test_cfg2_free_running(ge):
+    """The same 50 steps as independent trajectories: final loss and argmax of
+    the final weights on the last batch, reported; the GPU and the oracle
+    each round their own FP16 activations, so only drift is bounded."""
+    dims = datagen.mlp_dims_cfg2()
+    B, lr, mu = 4096, 0.05, 0.9
+    p0 = datagen.he_uniform_flat(dims)
+    tr = ge.MLPTrainer(dims, B, torch.float16, params=torch.from_numpy(p0).float().cuda())
+    w, v = p0.copy(), np.zeros_like(p0)
+    rels = []
+    for step in range(50):
+        X, y = datagen.template_images(B, 200, fmt="f16", batch=step)
+        tr.step(torch.from_numpy(X).half().cuda(), torch.from_numpy(y).cuda(), lr, mu)
+        ref = oracle.mlp_step(w, v, dims, X, y, lr, mu, plan="f16")
+        w, v = ref["params"], ref["vel"]
+        rels.append(abs(host(tr.loss)[0] - ref["loss"]) / ref["loss"])
+        if step % 10 == 9:
+            print(f"free-running step {step + 1}: loss rel diff {rels[-1]:.3e}", flush=True)
+    tr.step(torch.from_numpy(X).half().cuda(), torch.from_numpy(y).cuda(), 0.0, 0.0)
+    torch.cuda.synchronize()
+    Zg = host(tr.workspace_views(B)["Z"])
+    Zr = oracle.mlp_forward(w, dims, X, "f16")[2]
+    ok, nd = _argmax_ok(Zg, Zr)
+    print(f"784-2048-2048-10 free-running: final loss rel diff {rels[-1]:.3e}, worst {max(rels):.3e}; "
+          f"final argmax differs in {nd}/{B} rows ({int(np.count_nonzero(~ok))} outside the gap rule)")
+    assert max(rels) < 1e-2
+    assert np.count_nonzero(~ok) <= B // 1000
+
+
+def test_mlp_hidden_bias_from_dgrad_partials(ge):
+    """784-512-256-10 FP32 at batch 1024: the masked dgrad GEMMs take whole
+    64x64 tiles and write per-tile column partials, so db2 is formed from the
+    partials by the column-partial pass and db1 by the momentum update."""
+    dims = [784, 512, 256, 10]
+    B = 1024
+    X, y = datagen.template_images(B, 17, fmt="f32")
+    p0 = datagen.he_uniform_flat(dims)
+    tr = ge.MLPTrainer(dims, B, torch.float32, params=torch.from_numpy(p0).float().cuda())
+    for step in range(2):
+        w0, v0 = host(tr.params), host(tr.velocity)
+        tr.step(torch.from_numpy(X).float().cuda(), torch.from_numpy(y).cuda(), 0.1, 0.9)
+        _check_step(tr, dims, X, y, 0.1, 0.9, "f32", w0, v0, 1e-6, f"784-512-256-10 step {step}")
 
 
 def test_mlp_step_deterministic(ge):

@@ -225,3 +225,115 @@ def test_gru_f16_plan_close_to_f64():
     assert a["loss"] == pytest.approx(b["loss"], rel=1e-3)
     cos = a["grads"] @ b["grads"] / np.linalg.norm(a["grads"]) / np.linalg.norm(b["grads"])
     assert cos > 0.999
+
+
+# ------------------------------------------- stage-wise (given=) mode ------
+# The stage-wise mode feeds each stage the stored inputs it consumed.  Pins:
+# fed the oracle's own intermediates it reproduces the plain step exactly, and
+# a given tensor is only ever an input -- never handed back as an output.
+
+def _same(a, b, what):
+    if isinstance(a, (list, tuple)):
+        assert len(a) == len(b), what
+        for i, (x, y) in enumerate(zip(a, b)):
+            _same(x, y, f"{what}[{i}]")
+    elif a is None or isinstance(a, (int, float, np.integer, np.floating)):
+        assert a == b, what
+    else:
+        np.testing.assert_array_equal(np.asarray(a), np.asarray(b), err_msg=what)
+
+
+@pytest.mark.parametrize("plan,dims", [("f32", [30, 12, 9, 5]), ("f16", [24, 16, 8, 10])])
+def test_mlp_given_own_intermediates_reproduces_plain(plan, dims):
+    p = datagen.he_uniform_flat(dims)
+    g = np.random.default_rng(31)
+    X = datagen.representable(g.normal(size=(7, dims[0])), plan)
+    y = g.integers(0, dims[-1], size=7)
+    v = datagen.representable(g.normal(scale=1e-3, size=p.size), "f32")
+    plain = mlp_step(p, v, dims, X, y, 0.05, 0.9, plan=plan)
+    given = {"H": plain["H"], "Z": plain["Z"], "G": plain["G"], "dH": plain["dH"]}
+    staged = mlp_step(p, v, dims, X, y, 0.05, 0.9, plan=plan, given=given)
+    for k in ("loss", "row_loss", "Z", "G", "argmax", "H", "pre", "dH", "grads", "params", "vel",
+              "params_lowp"):
+        _same(staged[k], plain[k], k)
+
+
+def test_mlp_given_is_never_returned():
+    dims = [20, 9, 7, 6]
+    p = datagen.he_uniform_flat(dims)
+    g = np.random.default_rng(32)
+    X = g.normal(size=(5, 20))
+    y = g.integers(0, 6, size=5)
+    plain = mlp_step(p, np.zeros_like(p), dims, X, y, 0.0, 0.0, plan="f32")
+    # all 7s: layer 2's input and the loss stage's input are perturbed; the
+    # given Z's dominant column is one the oracle's own Z never picks
+    H = [plain["H"][0], np.full_like(plain["H"][1], 7.0)]
+    W3, b3 = mlp_unflatten(p, dims)[2]
+    col = int(np.argmin(np.full(7, 7.0) @ W3 + b3))
+    Zg = np.zeros_like(plain["Z"])
+    Zg[:, col] = 50.0
+    staged = mlp_step(p, np.zeros_like(p), dims, X, y, 0.0, 0.0, plan="f32",
+                      given={"H": H, "Z": Zg})
+    # returned H are the oracle's own layer outputs from the given inputs of
+    # each layer: H1 from X and H2 from the given H1 are unchanged
+    _same(staged["H"], plain["H"], "H")
+    assert not np.any(staged["H"][1] == 7.0)
+    # Z is the output layer applied to the given (perturbed) H2
+    assert not np.allclose(staged["Z"], plain["Z"])
+    ref_Z = np.asarray(np.float32(np.full((5, 7), 7.0) @ W3 + b3), np.float64)
+    np.testing.assert_allclose(staged["Z"], ref_Z, rtol=1e-6)
+    # argmax comes from the oracle's own Z, never from the given one
+    np.testing.assert_array_equal(staged["argmax"], staged["Z"].argmax(axis=1))
+    assert not np.any(staged["argmax"] == col)
+    # the loss stage is applied to the given Z: that column dominates every row
+    np.testing.assert_allclose(staged["row_loss"], np.where(y == col, 0.0, 50.0), atol=1e-12)
+
+
+def test_block_given_own_intermediates_reproduces_plain():
+    x, wu, wd, dy = datagen.block_inputs(24, D=16, F=40, seed=33)
+    plain = block_fwd_bwd(x, wu, wd, dy, fmt="bf16")
+    staged = block_fwd_bwd(x, wu, wd, dy, fmt="bf16",
+                           given={k: plain[k] for k in ("r", "n", "u", "a", "du", "dn")})
+    for k in plain:
+        _same(staged[k], plain[k], k)
+
+
+def test_block_given_is_never_returned():
+    x, wu, wd, dy = datagen.block_inputs(24, D=16, F=40, seed=34)
+    plain = block_fwd_bwd(x, wu, wd, dy, fmt="bf16")
+    staged = block_fwd_bwd(x, wu, wd, dy, fmt="bf16", given={"u": plain["u"] + 1.0})
+    _same(staged["u"], plain["u"], "u")
+    assert not np.array_equal(staged["du"], plain["du"])     # du consumes the given u
+
+
+def test_gru_given_own_intermediates_reproduces_plain():
+    H, V, Bn, T = 12, 20, 3, 5
+    P = datagen.gru_params(H, V)
+    tok = datagen.zipf_tokens(Bn, T + 1, seed=35, vocab=V)
+    flat = datagen.representable(gru_flatten(P), "f32")
+    v = np.zeros_like(flat)
+    plain = gru_step(flat, v, tok, H, V, 0.01, 0.9, plan="f16")
+    GH = np.concatenate([np.zeros((T * Bn, 2 * H)), plain["GHn"]], axis=1)
+    given = {"hs": plain["hs"], "R": plain["R"], "Z": plain["Zg"], "N": plain["N"], "GH": GH,
+             "rstd": plain["rstd"], "hn": plain["hn"], "logits": plain["logits"], "G": plain["G"],
+             "dhn": plain["dhn"], "dh_out": plain["dh_out"], "dGH": plain["dGH"],
+             "dGI": plain["dGI"], "dX": plain["dX"]}
+    staged = gru_step(flat, v, tok, H, V, 0.01, 0.9, plan="f16", given=given)
+    for k in plain:
+        _same(staged[k], plain[k], k)
+
+
+def test_gru_given_is_never_returned():
+    H, V, Bn, T = 12, 20, 3, 5
+    P = datagen.gru_params(H, V)
+    tok = datagen.zipf_tokens(Bn, T + 1, seed=36, vocab=V)
+    flat = datagen.representable(gru_flatten(P), "f32")
+    plain = gru_step(flat, np.zeros_like(flat), tok, H, V, 0.0, 0.0, plan="f16", update=False)
+    staged = gru_step(flat, np.zeros_like(flat), tok, H, V, 0.0, 0.0, plan="f16", update=False,
+                      given={"hs": plain["hs"] * 0.5, "logits": plain["logits"] + 3.0})
+    # the recurrence output at t=0 does not depend on a given h; later steps
+    # start from the given (halved) h_{t-1}, so they differ, but none equals it
+    _same(staged["hs"][:Bn], plain["hs"][:Bn], "hs t=0")
+    assert not np.allclose(staged["hs"][Bn:], plain["hs"][Bn:] * 0.5)
+    # logits are the classifier of the oracle's own hn of the given hs
+    assert not np.allclose(staged["logits"], plain["logits"] + 3.0)
