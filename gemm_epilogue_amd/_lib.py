@@ -77,12 +77,13 @@ SIGNATURES = {
     "ge_last_error": (C.c_char_p, []),
     "gemm_bias_act": (i32, [C.POINTER(GemmArgs), vp]),
     "gemm_workspace_bytes": (i64, [i32, i32, i64, i64, i64, i32]),
-    "colsum": (i32, [vp, i64, i64, i64, i32, f32, vp, vp, i64, vp]),
+    "colsum": (i32, [vp, i64, i64, i64, i32, f32, vp, i32, vp, i64, vp]),
     "colsum_workspace_bytes": (i64, [i64, i64]),
-    "softmax_xent_fwd_bwd": (i32, [vp, i64, i64, i64, vp, f32, vp, vp, vp, i64, i32, vp, vp]),
+    "softmax_xent_fwd_bwd": (i32, [vp, i64, i64, i64, vp, f32, vp, vp, vp, i64, i32, vp, vp, vp]),
     "rmsnorm_fwd_bwd": (i32, [C.POINTER(RmsnormArgs), vp]),
     "rmsnorm_workspace_bytes": (i64, [i64, i64]),
     "sgd_momentum": (i32, [vp, vp, vp, f32, f32, i64, vp, i32, vp]),
+    "params_to_lowp": (i32, [vp, vp, i64, i32, vp]),
     "mlp_param_count": (i64, [i32, C.POINTER(i64)]),
     "mlp_workspace_bytes": (i64, [C.POINTER(MlpDesc), i64]),
     "mlp_workspace_offsets": (i32, [C.POINTER(MlpDesc), i64, C.POINTER(i64), i32]),
@@ -90,7 +91,10 @@ SIGNATURES = {
     "mlp_block_workspace_bytes": (i64, [i64, i64, i64, i32]),
     "mlp_block_fwd_bwd": (i32, [C.POINTER(BlockArgs), vp]),
     "embedding_gather": (i32, [vp, i64, i64, i64, i32, vp, i64, vp, i64, i32, vp]),
-    "embedding_grad": (i32, [vp, i64, i32, vp, i64, i64, i64, f32, vp, i64, vp]),
+    "embedding_grad": (i32, [vp, i64, i32, vp, i64, i64, i64, f32, vp, i64, vp, i64, vp]),
+    "embedding_grad_workspace_bytes": (i64, [i64, i64]),
+    "gru_gates_fwd": (i32, [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]),
+    "gru_gates_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
     "gru_param_count": (i64, [i64, i64]),
     "gru_workspace_bytes": (i64, [C.POINTER(GruDesc)]),
     "gru_workspace_offsets": (i32, [C.POINTER(GruDesc), C.POINTER(i64), i32]),

@@ -89,18 +89,19 @@ int64_t colsum_workspace_bytes(int64_t M, int64_t N) {
 }
 
 int colsum(const void *X, int64_t M, int64_t N, int64_t ldx, int32_t x_type, float alpha, float *out,
-           void *workspace, int64_t workspace_bytes, ge_stream_t stream) {
+           int32_t accumulate, void *workspace, int64_t workspace_bytes, ge_stream_t stream) {
   CHECK(M >= 0 && N >= 0 && M < kMaxDim && N < kMaxDim, "colsum: bad size");
   CHECK(dtype_ok(x_type), "colsum: unknown x_type %d", x_type);
   if (N == 0) return GE_OK;
   CHECK(out != nullptr, "colsum: out is NULL");
   if (M > 0) CHECK(X != nullptr && ldx >= N, "colsum: X is NULL or ldx < N");
-  return colsum_launch(X, M, N, ldx, x_type, alpha, out, workspace, workspace_bytes, (hipStream_t)stream);
+  return colsum_launch(X, M, N, ldx, x_type, alpha, out, workspace, workspace_bytes, (hipStream_t)stream,
+                       accumulate != 0);
 }
 
 int softmax_xent_fwd_bwd(const float *logits, int64_t B, int64_t C, int64_t ld, const int32_t *labels,
                          float grad_scale, float *loss_mean, float *row_loss, void *dlogits, int64_t ld_d,
-                         int32_t d_type, int32_t *argmax, ge_stream_t stream) {
+                         int32_t d_type, int32_t *argmax, int32_t *bad_label_count, ge_stream_t stream) {
   CHECK(B >= 0 && B < kMaxDim, "softmax_xent_fwd_bwd: bad B");
   CHECK(C >= 1 && C <= 4096, "softmax_xent_fwd_bwd: C must be in [1, 4096]");
   CHECK(loss_mean != nullptr, "softmax_xent_fwd_bwd: loss_mean is NULL");
@@ -111,7 +112,7 @@ int softmax_xent_fwd_bwd(const float *logits, int64_t B, int64_t C, int64_t ld, 
     if (dlogits) CHECK(dtype_ok(d_type) && ld_d >= C, "softmax_xent_fwd_bwd: bad d_type / ld_d");
   }
   return xent_launch(logits, B, C, ld, labels, grad_scale, loss_mean, row_loss, dlogits, ld_d, d_type, argmax,
-                     (hipStream_t)stream);
+                     (hipStream_t)stream, bad_label_count);
 }
 
 int64_t rmsnorm_workspace_bytes(int64_t rows, int64_t D) {
@@ -146,6 +147,14 @@ int sgd_momentum(float *w, const float *g, float *v, float lr, float momentum, i
   if (w_lowp) CHECK(lowp_type == GE_F16 || lowp_type == GE_BF16, "sgd_momentum: lowp_type must be F16 or BF16");
   // without a gradient segment the update only reads g
   return sgd_launch(w, const_cast<float *>(g), v, lr, momentum, n, w_lowp, lowp_type, (hipStream_t)stream);
+}
+
+int params_to_lowp(const float *w, void *w_lowp, int64_t n, int32_t lowp_type, ge_stream_t stream) {
+  CHECK(n >= 0, "params_to_lowp: n < 0");
+  if (n == 0) return GE_OK;
+  CHECK(w != nullptr && w_lowp != nullptr, "params_to_lowp: NULL pointer");
+  CHECK(lowp_type == GE_F16 || lowp_type == GE_BF16, "params_to_lowp: lowp_type must be F16 or BF16");
+  return to_lowp_launch(w, n, w_lowp, lowp_type, (hipStream_t)stream);
 }
 
 }  // extern "C"

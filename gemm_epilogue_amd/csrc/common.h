@@ -109,7 +109,7 @@ int64_t gemm_colsum_bytes(int ab_type, int64_t M, int64_t N, int64_t K);
 int colsum_rows_launch(const float *part, int64_t rows, int64_t N, float alpha, float *out, hipStream_t st);
 int64_t gemm_ws_bytes(int layout, int ab_type, int64_t M, int64_t N, int64_t K, int split_k);
 int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int x_type, float alpha,
-                  float *out, void *ws, int64_t ws_bytes, hipStream_t s);
+                  float *out, void *ws, int64_t ws_bytes, hipStream_t s, int accumulate = 0);
 int64_t colsum_ws_bytes(int64_t M, int64_t N);
 // fused narrow output layer of the MLP step (head.hip)
 bool head_supported(int64_t B, int64_t D, int64_t C);
@@ -119,7 +119,8 @@ int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const fl
                 half_t *dH, float *db, float *db_below, float *loss, void *ws, hipStream_t st);
 int xent_launch(const float *logits, int64_t B, int64_t C, int64_t ld, const int32_t *labels,
                 float grad_scale, float *loss_mean, float *row_loss, void *dl, int64_t ld_d,
-                int d_type, int32_t *argmax, hipStream_t s);
+                int d_type, int32_t *argmax, hipStream_t s, int32_t *bad_label_count = nullptr);
+int to_lowp_launch(const float *w, int64_t n, void *w_lowp, int lowp_type, hipStream_t s);
 int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t s);
 int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D);
 // seg_part (optional): g[seg_g0 .. seg_g0 + seg_len) is first set to

@@ -26,8 +26,10 @@ int tokens_time_major_launch(const int32_t *tok, int B, int T, int32_t *inp, int
 int fill_zero_launch(void *p, int64_t bytes, hipStream_t s);
 int embedding_gather_launch(const void *table, int64_t V, int64_t H, int64_t ldt, int tt, const int32_t *idx,
                             int64_t n, void *out, int64_t ldo, int ot, hipStream_t s);
+int64_t embedding_grad_ws_bytes(int64_t n, int64_t V);
 int embedding_grad_launch(const void *dX, int64_t ldx, int xt, const int32_t *idx, int64_t n, int64_t V,
-                          int64_t H, float alpha, float *dE, int64_t lde, hipStream_t s);
+                          int64_t H, float alpha, float *dE, int64_t lde, void *ws, int64_t ws_bytes,
+                          hipStream_t s);
 int gru_fwd_launch(const float *GI, const float *GH, const float *hp, int B, int H, float *R, float *Z, float *N,
                    float *h, half_t *h16, hipStream_t s);
 int gru_bwd_launch(const float *dh_out, const float *carry, const float *R, const float *Z, const float *N,
@@ -64,7 +66,7 @@ bool desc_ok(const ge_gru_desc *d) {
 // byte offsets of every workspace region, in GE_GRU_WS_* order
 struct GruLayout {
   int64_t off[GE_GRU_WS_COUNT];
-  int64_t gemm_off, gemm_ws, cs_off, cs_ws, total;
+  int64_t gemm_off, gemm_ws, cs_off, cs_ws, emb_off, emb_ws, total;
 };
 
 GruLayout layout_of(const ge_gru_desc *d) {
@@ -116,6 +118,9 @@ GruLayout layout_of(const ge_gru_desc *d) {
   L.cs_off = o;
   L.cs_ws = std::max(colsum_ws_bytes(NT, V), colsum_ws_bytes(NT, H3));
   o = align_up(o + L.cs_ws);
+  L.emb_off = o;
+  L.emb_ws = embedding_grad_ws_bytes(NT, V);
+  o = align_up(o + L.emb_ws);
   L.total = o;
   return L;
 }
@@ -158,14 +163,45 @@ int embedding_gather(const void *table, int64_t V, int64_t H, int64_t ld_table, 
   return embedding_gather_launch(table, V, H, ld_table, type, idx, n, out, ld_out, out_type, (hipStream_t)stream);
 }
 
+int64_t embedding_grad_workspace_bytes(int64_t n, int64_t V) {
+  if (n < 0 || V < 0) return -1;
+  return embedding_grad_ws_bytes(n, V);
+}
+
 int embedding_grad(const void *dX, int64_t ld_dx, int32_t dx_type, const int32_t *idx, int64_t n, int64_t V,
-                   int64_t H, float alpha, float *dE, int64_t ld_de, ge_stream_t stream) {
-  CHECK(V >= 0 && H >= 0 && n >= 0 && V < (1 << 20) && H < (1 << 30) && n < (1 << 30),
-        "embedding_grad: bad sizes");
+                   int64_t H, float alpha, float *dE, int64_t ld_de, void *workspace, int64_t workspace_bytes,
+                   ge_stream_t stream) {
+  CHECK(V >= 0 && H >= 0 && n >= 0 && V <= 16384 && H < (1 << 30) && n < (1 << 30),
+        "embedding_grad: bad sizes (V <= 16384)");
   CHECK(dtype_ok(dx_type), "embedding_grad: unknown type");
   if (V == 0 || H == 0) return GE_OK;
   CHECK(dE && ld_de >= H && (n == 0 || (dX && idx && ld_dx >= H)), "embedding_grad: NULL pointer or ld < H");
-  return embedding_grad_launch(dX, ld_dx, dx_type, idx, n, V, H, alpha, dE, ld_de, (hipStream_t)stream);
+  return embedding_grad_launch(dX, ld_dx, dx_type, idx, n, V, H, alpha, dE, ld_de, workspace, workspace_bytes,
+                               (hipStream_t)stream);
+}
+
+int gru_gates_fwd(const float *GI, const float *GH, const float *h_prev, int64_t B, int64_t H, float *r, float *z,
+                  float *n, float *h, void *h_f16, ge_stream_t stream) {
+  CHECK(B >= 0 && H >= 0 && B * H < ((int64_t)1 << 31) && H % 4 == 0, "gru_gates_fwd: bad sizes (H %% 4 == 0)");
+  if (B == 0 || H == 0) return GE_OK;
+  CHECK(GI && GH && r && z && n && h, "gru_gates_fwd: NULL pointer");
+  const void *ps[] = {GI, GH, h_prev, r, z, n, h};
+  for (const void *p : ps) CHECK((uintptr_t)p % 16 == 0, "gru_gates_fwd: pointers must be 16-byte aligned");
+  CHECK((uintptr_t)h_f16 % 8 == 0, "gru_gates_fwd: h_f16 must be 8-byte aligned");
+  return gru_fwd_launch(GI, GH, h_prev, (int)B, (int)H, r, z, n, h, (half_t *)h_f16, (hipStream_t)stream);
+}
+
+int gru_gates_bwd(const float *dh_out, const float *carry, const float *r, const float *z, const float *n,
+                  const float *GH, const float *h_prev, int64_t B, int64_t H, void *dGH, void *dGI, float *dh_dir,
+                  ge_stream_t stream) {
+  CHECK(B >= 0 && H >= 0 && B * H < ((int64_t)1 << 31) && H % 4 == 0, "gru_gates_bwd: bad sizes (H %% 4 == 0)");
+  if (B == 0 || H == 0) return GE_OK;
+  CHECK(dh_out && r && z && n && GH && dGH && dGI && dh_dir, "gru_gates_bwd: NULL pointer");
+  const void *ps[] = {dh_out, carry, r, z, n, GH, h_prev, dh_dir};
+  for (const void *p : ps) CHECK((uintptr_t)p % 16 == 0, "gru_gates_bwd: pointers must be 16-byte aligned");
+  CHECK((uintptr_t)dGH % 8 == 0 && (uintptr_t)dGI % 8 == 0, "gru_gates_bwd: dGH, dGI must be 8-byte aligned");
+  return gru_bwd_launch(dh_out, carry, r, z, n, GH, h_prev, (int)B, (int)H, (half_t *)dGH, (half_t *)dGI, dh_dir,
+                        (hipStream_t)stream);
 }
 
 int64_t gru_param_count(int64_t V, int64_t H) {
@@ -308,7 +344,7 @@ int gru_lm_train_step(const ge_gru_desc *desc, const ge_gru_buffers *buf, const 
   RUN(colsum_launch(dGI, NT, H3, H3, GE_F16, alpha, gr + obi, cws, L.cs_ws, s));
   g = gargs(GE_NT, NT, H, H3, dGI, H3, lp + oWi, H3, DX, H, GE_F32, gws, L.gemm_ws);
   RUN(gemm_launch(g, s));
-  RUN(embedding_grad_launch(DX, H, GE_F32, inp, NT, V, H, alpha, gr + oE, H, s));
+  RUN(embedding_grad_launch(DX, H, GE_F32, inp, NT, V, H, alpha, gr + oE, H, ws + L.emb_off, L.emb_ws, s));
   return sgd_launch(buf->params, buf->grads, buf->velocity, lr, momentum, P, buf->params_lowp, GE_F16, s);
 }
 

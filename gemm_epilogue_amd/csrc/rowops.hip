@@ -55,7 +55,7 @@ __device__ __forceinline__ void cs_load8(const T *__restrict__ X, int64_t i, boo
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const T *__restrict__ X, int M, int N, int64_t ldx,
                                                              int vec, int rows_per, float alpha,
-                                                             float *__restrict__ out) {
+                                                             float *__restrict__ out, int accumulate) {
   __shared__ float red[3][CS_COLS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = blockIdx.x * CS_COLS + lane * CS_VEC;
@@ -93,13 +93,13 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T *__restrict
     for (int j = 0; j < 8; ++j) {
       const int c = lane * CS_VEC + j;
       const float t = ((s[j] + red[0][c]) + red[1][c]) + red[2][c];
-      if (n + j < N) dst[n + j] = alpha * t;
+      if (n + j < N) dst[n + j] = accumulate ? dst[n + j] + alpha * t : alpha * t;
     }
   }
 }
 
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restrict__ part, int splits, int N,
-                                                           float alpha, float *__restrict__ out) {
+                                                           float alpha, float *__restrict__ out, int accumulate) {
   __shared__ float red[3][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = blockIdx.x * 64 + lane;
@@ -117,7 +117,10 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restri
   }
   if (wave > 0) red[wave - 1][lane] = s;
   __syncthreads();
-  if (wave == 0 && n < N) out[n] = alpha * (((s + red[0][lane]) + red[1][lane]) + red[2][lane]);
+  if (wave == 0 && n < N) {
+    const float t = alpha * (((s + red[0][lane]) + red[1][lane]) + red[2][lane]);
+    out[n] = accumulate ? out[n] + t : t;
+  }
 }
 
 namespace {
@@ -131,23 +134,23 @@ int colsum_splits(int64_t M, int64_t N) {
 
 template <typename T>
 void colsum_partial(dim3 grid, hipStream_t st, const void *X, int M, int N, int64_t ldx, int vec, int rows_per,
-                    float alpha, float *out) {
+                    float alpha, float *out, int acc) {
   hipLaunchKernelGGL(colsum_partial_kernel<T>, grid, dim3(256), 0, st, (const T *)X, M, N, ldx, vec, rows_per,
-                     alpha, out);
+                     alpha, out, acc);
 }
 
 void colsum_partial_any(int xt, dim3 grid, hipStream_t st, const void *X, int M, int N, int64_t ldx, int vec,
-                        int rows_per, float alpha, float *out) {
-  if (xt == GE_F32) colsum_partial<float>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out);
-  else if (xt == GE_F16) colsum_partial<half_t>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out);
-  else colsum_partial<bf16_t>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out);
+                        int rows_per, float alpha, float *out, int acc) {
+  if (xt == GE_F32) colsum_partial<float>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out, acc);
+  else if (xt == GE_F16) colsum_partial<half_t>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out, acc);
+  else colsum_partial<bf16_t>(grid, st, X, M, N, ldx, vec, rows_per, alpha, out, acc);
 }
 }  // namespace
 
 int colsum_rows_launch(const float *part, int64_t rows, int64_t N, float alpha, float *out, hipStream_t st) {
   if (N == 0) return GE_OK;
   hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, part, (int)rows,
-                     (int)N, alpha, out);
+                     (int)N, alpha, out, 0);
   return launch_status("colsum (rows)");
 }
 
@@ -158,14 +161,14 @@ int64_t colsum_ws_bytes(int64_t M, int64_t N) {
 }
 
 int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt, float alpha, float *out,
-                  void *ws, int64_t ws_bytes, hipStream_t st) {
+                  void *ws, int64_t ws_bytes, hipStream_t st, int accumulate) {
   if (N == 0) return GE_OK;
   const int vec = vec_aligned(X, ldx, dtype_size(xt), 16);
   const int colblocks = (int)((N + CS_COLS - 1) / CS_COLS);
   const int splits = M > 0 ? colsum_splits(M, N) : 1;
   if (splits == 1) {
     colsum_partial_any(xt, dim3(colblocks, 1), st, X, (int)M, (int)N, ldx, vec, (int)std::max<int64_t>(M, 1),
-                       alpha, out);
+                       alpha, out, accumulate);
     return launch_status("colsum");
   }
   const int64_t need = (int64_t)splits * N * 4;
@@ -174,11 +177,11 @@ int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt, floa
     return GE_E_WORKSPACE;
   }
   const int rows_per = (int)((M + splits - 1) / splits);
-  colsum_partial_any(xt, dim3(colblocks, splits), st, X, (int)M, (int)N, ldx, vec, rows_per, 1.0f, (float *)ws);
+  colsum_partial_any(xt, dim3(colblocks, splits), st, X, (int)M, (int)N, ldx, vec, rows_per, 1.0f, (float *)ws, 0);
   int s = launch_status("colsum (partial)");
   if (s != GE_OK) return s;
   hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st,
-                     (const float *)ws, splits, (int)N, alpha, out);
+                     (const float *)ws, splits, (int)N, alpha, out, accumulate);
   return launch_status("colsum (final)");
 }
 
@@ -241,31 +244,46 @@ __global__ __launch_bounds__(256) void xent_rows_kernel(const float *__restrict_
 }
 
 // mean of the row losses: one block, fixed order (thread t sums rows t, t+256,
-// ..., then a fixed tree over the 256 partials).
+// ..., then a fixed tree over the 256 partials).  With `bad` it also counts
+// the labels outside [0, C) (an integer count, so the order does not matter).
 __global__ __launch_bounds__(256) void xent_mean_kernel(const float *__restrict__ row_loss, int B,
-                                                        float *__restrict__ out) {
+                                                        float *__restrict__ out, const int32_t *__restrict__ labels,
+                                                        int C, int32_t *__restrict__ bad) {
   __shared__ float red[256];
+  __shared__ int nbad[256];
   float s = 0.f;
-  for (int i = threadIdx.x; i < B; i += 256) s += row_loss[i];
+  int nb = 0;
+  for (int i = threadIdx.x; i < B; i += 256) {
+    s += row_loss[i];
+    if (bad) nb += (unsigned)labels[i] >= (unsigned)C;
+  }
   red[threadIdx.x] = s;
+  nbad[threadIdx.x] = nb;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    if ((int)threadIdx.x < w) {
+      red[threadIdx.x] += red[threadIdx.x + w];
+      nbad[threadIdx.x] += nbad[threadIdx.x + w];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[0] = B > 0 ? red[0] / (float)B : 0.f;
+  if (threadIdx.x == 0) {
+    out[0] = B > 0 ? red[0] / (float)B : 0.f;
+    if (bad) bad[0] = nbad[0];
+  }
 }
 
 int xent_launch(const float *Z, int64_t B, int64_t C, int64_t ld, const int32_t *labels, float gscale,
                 float *loss_mean, float *row_loss, void *dZ, int64_t ldd, int dt, int32_t *amax,
-                hipStream_t st) {
+                hipStream_t st, int32_t *bad_label_count) {
   if (B > 0) {
     hipLaunchKernelGGL(xent_rows_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, st, Z, (int)B, (int)C,
                        ld, labels, gscale, row_loss, dZ, ldd, dt, amax);
     int s = launch_status("softmax_xent_fwd_bwd (rows)");
     if (s != GE_OK) return s;
   }
-  hipLaunchKernelGGL(xent_mean_kernel, dim3(1), dim3(256), 0, st, row_loss, (int)B, loss_mean);
+  hipLaunchKernelGGL(xent_mean_kernel, dim3(1), dim3(256), 0, st, row_loss, (int)B, loss_mean, labels, (int)C,
+                     bad_label_count);
   return launch_status("softmax_xent_fwd_bwd (mean)");
 }
 
@@ -528,6 +546,32 @@ int sgd_launch(float *w, float *g, float *v, float lr, float mu, int64_t n, void
   }
   hipLaunchKernelGGL(sgd_kernel, dim3(blocks), dim3(256), 0, st, w, g, v, lr, mu, n, wl, lt, vec, sg);
   return launch_status("sgd_momentum");
+}
+
+// ======================= low-precision working copy =========================
+// w_lowp[i] = convert(w[i]) with round-to-nearest-even: the copy the update
+// keeps in step, formed here for the initial parameters.
+__global__ __launch_bounds__(256) void to_lowp_kernel(const float *__restrict__ w, int64_t n, void *__restrict__ wl,
+                                                      int lt, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (vec && i + 3 < n) {
+      const f32x4 x = *(const f32x4 *)(w + i);
+      const float o[4] = {x[0], x[1], x[2], x[3]};
+      store4_any(wl, i, lt, true, o);
+    } else {
+      for (int64_t k = i; k < n && k < i + 4; ++k) store_any(wl, k, lt, w[k]);
+    }
+  }
+}
+
+int to_lowp_launch(const float *w, int64_t n, void *wl, int lt, hipStream_t st) {
+  if (n == 0) return GE_OK;
+  const int vec = ((uintptr_t)w % 16 == 0) && ((uintptr_t)wl % 8 == 0);
+  const int64_t items = (n + 3) / 4;
+  const unsigned blocks = (unsigned)std::min<int64_t>((items + 255) / 256, 2048);
+  hipLaunchKernelGGL(to_lowp_kernel, dim3(blocks), dim3(256), 0, st, w, n, wl, lt, vec);
+  return launch_status("params_to_lowp");
 }
 
 }  // namespace ge

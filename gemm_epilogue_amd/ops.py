@@ -93,21 +93,24 @@ def gemm_bias_act(A, B, layout: str = "NN", *, out=None, out_dtype=torch.float32
     return out
 
 
-def colsum(X, alpha: float = 1.0, *, out=None, workspace=None):
-    """out[n] = alpha * sum_m X[m, n]  (f32)."""
+def colsum(X, alpha: float = 1.0, *, out=None, accumulate: bool = False, workspace=None):
+    """out[n] = alpha * sum_m X[m, n] (f32); with accumulate, added to out."""
     M, N = X.shape
     if out is None:
         out = torch.empty(N, dtype=torch.float32, device=X.device)
     ws = _workspace(int(lib.colsum_workspace_bytes(M, N)), X.device, workspace)
-    check(lib.colsum(_ptr(X), M, N, _ld(X), dtype_code(X.dtype), alpha, _ptr(out), _ptr(ws),
+    if accumulate and (out is None or out.dtype != torch.float32):
+        raise ValueError("accumulate needs an f32 out tensor")
+    check(lib.colsum(_ptr(X), M, N, _ld(X), dtype_code(X.dtype), alpha, _ptr(out), int(accumulate), _ptr(ws),
                      0 if ws is None else ws.numel() * ws.element_size(), _stream()), "colsum")
     return out
 
 
 def softmax_xent_fwd_bwd(logits, labels, grad_scale: float, *, d_dtype=torch.float32,
                          want_grad=True, want_argmax=True, loss=None, row_loss=None, dlogits=None,
-                         argmax=None):
-    """Returns (loss_mean[1], row_loss[B], dlogits or None, argmax or None)."""
+                         argmax=None, bad_label_count=None):
+    """Returns (loss_mean[1], row_loss[B], dlogits or None, argmax or None);
+    bad_label_count (device int32 [1]) receives the number of labels outside [0, C)."""
     B, Cn = logits.shape
     dev = logits.device
     loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
@@ -119,7 +122,8 @@ def softmax_xent_fwd_bwd(logits, labels, grad_scale: float, *, d_dtype=torch.flo
     check(lib.softmax_xent_fwd_bwd(
         _ptr(logits), B, Cn, _ld(logits), _ptr(labels), grad_scale, _ptr(loss), _ptr(row_loss),
         _ptr(dlogits), 0 if dlogits is None else _ld(dlogits),
-        GE_F32 if dlogits is None else dtype_code(dlogits.dtype), _ptr(argmax), _stream()),
+        GE_F32 if dlogits is None else dtype_code(dlogits.dtype), _ptr(argmax), _ptr(bad_label_count),
+        _stream()),
         "softmax_xent_fwd_bwd")
     return loss, row_loss, dlogits, argmax
 
@@ -195,7 +199,10 @@ class MLPTrainer:
             self.params.copy_(params)
         self.grads = torch.zeros(P, dtype=torch.float32, device=device)
         self.velocity = torch.zeros(P, dtype=torch.float32, device=device)
-        self.params_lowp = (self.params.to(torch.float16) if storage == torch.float16 else None)
+        self.params_lowp = None
+        if storage == torch.float16:
+            self.params_lowp = torch.empty(P, dtype=torch.float16, device=device)
+            params_to_lowp(self.params, self.params_lowp)
         nbytes = int(lib.mlp_workspace_bytes(C.byref(self.desc), batch))
         check(0 if nbytes >= 0 else -1, "mlp_workspace_bytes")
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
@@ -207,7 +214,7 @@ class MLPTrainer:
 
     def sync_lowp(self):
         if self.params_lowp is not None:
-            self.params_lowp.copy_(self.params.to(torch.float16))
+            params_to_lowp(self.params, self.params_lowp)
 
     def step(self, X, labels, lr: float, momentum: float, batch=None):
         B = X.shape[0] if batch is None else batch
@@ -304,12 +311,52 @@ def embedding_gather(table, idx, *, out=None, out_dtype=None):
     return out
 
 
-def embedding_grad(dX, idx, V: int, alpha: float = 1.0, *, out=None):
+def embedding_grad(dX, idx, V: int, alpha: float = 1.0, *, out=None, workspace=None):
     n, H = dX.shape
     out = torch.empty((V, H), dtype=torch.float32, device=dX.device) if out is None else out
+    ws = _workspace(int(lib.embedding_grad_workspace_bytes(n, V)), dX.device, workspace)
     check(lib.embedding_grad(_ptr(dX), _ld(dX), dtype_code(dX.dtype), _ptr(idx), n, V, H, alpha,
-                             _ptr(out), _ld(out), _stream()), "embedding_grad")
+                             _ptr(out), _ld(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+          "embedding_grad")
     return out
+
+
+def params_to_lowp(w, w_lowp):
+    """w_lowp = convert(w), round to nearest even (the GEMMs' working copy)."""
+    if w.dtype != torch.float32 or w_lowp.numel() != w.numel():
+        raise ValueError("params_to_lowp: f32 source and a working copy of the same size")
+    check(lib.params_to_lowp(_ptr(w), _ptr(w_lowp), w.numel(), dtype_code(w_lowp.dtype), _stream()),
+          "params_to_lowp")
+    return w_lowp
+
+
+def gru_gates_fwd(GI, GH, h_prev, *, r=None, z=None, n=None, h=None, h_f16=None):
+    """One GRU timestep's gates (see gru_gates_fwd in the header); h_prev None = h_0 = 0.
+    Returns (r, z, n, h, h_f16)."""
+    B, H3 = GI.shape
+    H = H3 // 3
+    dev = GI.device
+
+    def mk(t, dt=torch.float32):
+        return torch.empty((B, H), dtype=dt, device=dev) if t is None else t
+
+    r, z, n, h = mk(r), mk(z), mk(n), mk(h)
+    check(lib.gru_gates_fwd(_ptr(GI), _ptr(GH), _ptr(h_prev), B, H, _ptr(r), _ptr(z), _ptr(n), _ptr(h),
+                            _ptr(h_f16), _stream()), "gru_gates_fwd")
+    return r, z, n, h, h_f16
+
+
+def gru_gates_bwd(dh_out, carry, r, z, n, GH, h_prev, *, dGH=None, dGI=None, dh_dir=None):
+    """One GRU timestep's gate backward (see gru_gates_bwd in the header); carry or
+    h_prev None = 0.  Returns (dGH f16, dGI f16, dh_dir f32)."""
+    B, H = dh_out.shape
+    dev = dh_out.device
+    dGH = torch.empty((B, 3 * H), dtype=torch.float16, device=dev) if dGH is None else dGH
+    dGI = torch.empty((B, 3 * H), dtype=torch.float16, device=dev) if dGI is None else dGI
+    dh_dir = torch.empty((B, H), dtype=torch.float32, device=dev) if dh_dir is None else dh_dir
+    check(lib.gru_gates_bwd(_ptr(dh_out), _ptr(carry), _ptr(r), _ptr(z), _ptr(n), _ptr(GH), _ptr(h_prev), B, H,
+                            _ptr(dGH), _ptr(dGI), _ptr(dh_dir), _stream()), "gru_gates_bwd")
+    return dGH, dGI, dh_dir
 
 
 def gru_param_count(V: int, H: int) -> int:
@@ -334,7 +381,8 @@ class GRUTrainer:
             self.params.copy_(params)
         self.grads = torch.zeros(P, dtype=torch.float32, device=device)
         self.velocity = torch.zeros(P, dtype=torch.float32, device=device)
-        self.params_lowp = self.params.to(torch.float16)
+        self.params_lowp = torch.empty(P, dtype=torch.float16, device=device)
+        params_to_lowp(self.params, self.params_lowp)
         nbytes = int(lib.gru_workspace_bytes(C.byref(self.desc)))
         if nbytes < 0:
             raise ValueError("bad GRU sizes (V <= 4096, 4 <= H <= 4096, H % 4 == 0)")

@@ -136,7 +136,8 @@ int64_t gemm_workspace_bytes(int32_t layout, int32_t ab_type, int64_t M, int64_t
                              int64_t K, int32_t split_k);
 
 /* ------------------------------------------------------------------------
- * colsum -- out[n] = alpha * sum_m X[m, n]   (bias gradients)
+ * colsum -- out[n] = alpha * sum_m X[m, n]            (accumulate == 0)
+ *           out[n] = out[n] + alpha * sum_m X[m, n]   (accumulate != 0)
  * [CAP] "Work through the backward pass" / "Check your mapping": each db is
  * a column reduction over the batch.  X: device [M x N] (x_type, ldx >= N);
  * out: device f32 [N].  Sums in FP32 in a fixed order.  Problems with many
@@ -144,7 +145,8 @@ int64_t gemm_workspace_bytes(int32_t layout, int32_t ab_type, int64_t M, int64_t
  * (colsum_workspace_bytes(M, N) bytes; 0 means none needed).
  * ---------------------------------------------------------------------- */
 int colsum(const void *X, int64_t M, int64_t N, int64_t ldx, int32_t x_type, float alpha,
-           float *out, void *workspace, int64_t workspace_bytes, ge_stream_t stream);
+           float *out, int32_t accumulate, void *workspace, int64_t workspace_bytes,
+           ge_stream_t stream);
 int64_t colsum_workspace_bytes(int64_t M, int64_t N);
 
 /* ------------------------------------------------------------------------
@@ -158,15 +160,18 @@ int64_t colsum_workspace_bytes(int64_t M, int64_t N);
  *   loss_mean[0] = (1/B) sum_b row_loss[b]      (fixed-order sum)
  *   argmax[b] = lowest index of the row maximum  (optional)
  * logits: device f32 [B x C] (ld >= C); labels: device int32 [B] in [0, C)
- * (a label outside that range reads nothing and gives a NaN row loss);
- * row_loss: device f32 [B] (required: it is also the scratch of the mean);
- * loss_mean: device f32 [1]; dlogits: device [B x C] (d_type, ld_d) or NULL;
- * argmax: device int32 [B] or NULL.  C <= 4096.
+ * (a label outside that range reads nothing and gives a NaN row loss, so the
+ * mean is NaN too); row_loss: device f32 [B] (required: it is also the
+ * scratch of the mean); loss_mean: device f32 [1]; dlogits: device [B x C]
+ * (d_type, ld_d) or NULL; argmax: device int32 [B] or NULL;
+ * bad_label_count: device int32 [1] or NULL, receives the number of labels
+ * outside [0, C) (written, not accumulated; labels are device data, so this
+ * is how a caller learns of them without a host check).  C <= 4096.
  * ---------------------------------------------------------------------- */
 int softmax_xent_fwd_bwd(const float *logits, int64_t B, int64_t C, int64_t ld,
                          const int32_t *labels, float grad_scale, float *loss_mean,
                          float *row_loss, void *dlogits, int64_t ld_d, int32_t d_type,
-                         int32_t *argmax, ge_stream_t stream);
+                         int32_t *argmax, int32_t *bad_label_count, ge_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * rmsnorm_fwd_bwd -- RMSNorm over rows of width D, FP32 statistics
@@ -220,6 +225,14 @@ int64_t rmsnorm_workspace_bytes(int64_t rows, int64_t D);
  * ---------------------------------------------------------------------- */
 int sgd_momentum(float *w, const float *g, float *v, float lr, float momentum, int64_t n,
                  void *w_lowp, int32_t lowp_type, ge_stream_t stream);
+
+/* params_to_lowp -- w_lowp[i] = convert(w[i]), round to nearest even: the
+ * low-precision working copy of a flat parameter buffer that the GEMMs read
+ * ([CAT] "The Debugging Lesson Was Numerical": FP16 only as GEMM input), as
+ * sgd_momentum keeps it after each update; used to form it from the initial
+ * FP32 parameters.  w: device f32 [n]; w_lowp: device [n] of lowp_type
+ * (F16 or BF16). */
+int params_to_lowp(const float *w, void *w_lowp, int64_t n, int32_t lowp_type, ge_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * mlp_train_step -- one SGD-momentum step of a dense ReLU MLP
@@ -308,15 +321,53 @@ int mlp_block_fwd_bwd(const ge_block_args *args, ge_stream_t stream);
  * embedding_gather: out[i, :] = table[idx[i], :] for i < n; table [V x H]
  * (type, ld_table), out [n x H] (out_type, ld_out); an index outside [0, V)
  * yields a zero row (nothing is read for it).
- * embedding_grad: dE[v, :] = alpha * sum over i with idx[i] == v of dX[i, :],
- * summed in increasing i (deterministic); every row of dE [V x H] (f32,
- * ld_de) is written, rows with no occurrence get zeros.
+ * embedding_grad: dE[v, :] = alpha * sum over i with idx[i] == v of dX[i, :];
+ * every row of dE [V x H] (f32, ld_de) is written, rows with no occurrence
+ * get zeros; an index outside [0, V) contributes nothing.  The positions are
+ * first ordered by index value (a stable counting sort into `workspace`,
+ * embedding_grad_workspace_bytes(n, V) bytes), then each row of dE is the sum
+ * of its run, taken in 16 contiguous pieces of increasing i added in order:
+ * a fixed order, so the result is deterministic, and dX is read once
+ * (O(n H + V H) work).  V <= 16384.
  * ---------------------------------------------------------------------- */
 int embedding_gather(const void *table, int64_t V, int64_t H, int64_t ld_table, int32_t type,
                      const int32_t *idx, int64_t n, void *out, int64_t ld_out, int32_t out_type,
                      ge_stream_t stream);
 int embedding_grad(const void *dX, int64_t ld_dx, int32_t dx_type, const int32_t *idx, int64_t n,
-                   int64_t V, int64_t H, float alpha, float *dE, int64_t ld_de, ge_stream_t stream);
+                   int64_t V, int64_t H, float alpha, float *dE, int64_t ld_de, void *workspace,
+                   int64_t workspace_bytes, ge_stream_t stream);
+int64_t embedding_grad_workspace_bytes(int64_t n, int64_t V);
+
+/* ------------------------------------------------------------------------
+ * GRU gate arithmetic of one timestep, forward and backward
+ * [CAT] "The Work Moved Down a Layer" (the GRU gate shader of the recurrent
+ * trainer), "The Debugging Lesson Was Numerical" (recurrent state and gate
+ * math in FP32, FP16 only for GEMM inputs).  The pages print no equations;
+ * the cell is the standard one (gate blocks r, z, n along 3H, the hidden
+ * bias inside the reset product, which the caller's GH already holds):
+ * gru_gates_fwd, per batch row b and unit j:
+ *   r = sigmoid(GI_r + GH_r);  z = sigmoid(GI_z + GH_z);
+ *   n = tanh(GI_n + r GH_n);   h = (1 - z) n + z h_prev
+ * GI, GH: device f32 [B x 3H] (row b = [r | z | n] blocks, GI = x W_i + b_i,
+ * GH = h_prev W_h + b_h); h_prev: device f32 [B x H] or NULL (h_0 = 0);
+ * outputs r, z, n, h: device f32 [B x H] (r, z, n are kept for the
+ * backward); h_f16: device f16 [B x H] copy of h for the next recurrent
+ * GEMM, or NULL.
+ * gru_gates_bwd, with dh = dh_out + carry (carry: gradient reaching h from
+ * the next timestep, NULL = 0) and the same r, z, n, GH, h_prev:
+ *   dn = dh (1 - z);  dz = dh (h_prev - n);  dh_dir = dh z;
+ *   dnh = dn (1 - n^2);  dGr = dnh GH_n r (1 - r);  dGz = dz z (1 - z);
+ *   dGH = [dGr | dGz | dnh r],  dGI = [dGr | dGz | dnh]
+ * dGH, dGI: device f16 [B x 3H] (GEMM inputs of the carry and weight
+ * gradients); dh_dir: device f32 [B x H] (the part of dh_prev that bypasses
+ * W_h).  All rows contiguous; H % 4 == 0; f32 pointers 16-byte aligned,
+ * f16 pointers 8-byte aligned (GE_E_INVALID otherwise).
+ * ---------------------------------------------------------------------- */
+int gru_gates_fwd(const float *GI, const float *GH, const float *h_prev, int64_t B, int64_t H,
+                  float *r, float *z, float *n, float *h, void *h_f16, ge_stream_t stream);
+int gru_gates_bwd(const float *dh_out, const float *carry, const float *r, const float *z,
+                  const float *n, const float *GH, const float *h_prev, int64_t B, int64_t H,
+                  void *dGH, void *dGI, float *dh_dir, ge_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * gru_lm_train_step -- one training step of a byte-level GRU language model

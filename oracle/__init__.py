@@ -38,12 +38,13 @@ from .ops import (act_forward, act_backward_factor, gemm_epilogue, colsum,
 from .mlp import (mlp_param_count, mlp_unflatten, mlp_step, mlp_forward,
                   mlp_loss_only)
 from .block import block_fwd_bwd
-from .gru import gru_param_count, gru_flatten, gru_unflatten, gru_step, gru_loss_only
+from .gru import (gru_param_count, gru_flatten, gru_unflatten, gru_step, gru_loss_only,
+                  gru_gates_fwd, gru_gates_bwd)
 
 __all__ = [
     "round_fmt", "FORMATS", "act_forward", "act_backward_factor",
     "gemm_epilogue", "colsum", "softmax_xent", "rmsnorm_fwd", "rmsnorm_bwd",
     "sgd_momentum", "mlp_param_count", "mlp_unflatten", "mlp_step",
     "mlp_forward", "mlp_loss_only", "block_fwd_bwd", "gru_param_count",
-    "gru_flatten", "gru_unflatten", "gru_step", "gru_loss_only",
+    "gru_flatten", "gru_unflatten", "gru_step", "gru_loss_only", "gru_gates_fwd", "gru_gates_bwd",
 ]

@@ -65,6 +65,47 @@ def _sigmoid(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
+def gru_gates_fwd(GI, GH, h_prev):
+    """Gate arithmetic of one forward timestep (the GRU gate stage of the
+    recurrent trainer in "The Work Moved Down a Layer"; standard cell):
+
+        r = sigmoid(GI_r + GH_r);  z = sigmoid(GI_z + GH_z)
+        n = tanh(GI_n + r * GH_n); h = (1 - z) * n + z * h_prev
+
+    GI, GH: [B x 3H] with column blocks (r | z | n); returns (r, z, n, h),
+    float64, unrounded.
+    """
+    GI = np.asarray(GI, dtype=np.float64)
+    GH = np.asarray(GH, dtype=np.float64)
+    h_prev = np.asarray(h_prev, dtype=np.float64)
+    H = h_prev.shape[1]
+    r = _sigmoid(GI[:, :H] + GH[:, :H])
+    z = _sigmoid(GI[:, H:2 * H] + GH[:, H:2 * H])
+    n = np.tanh(GI[:, 2 * H:] + r * GH[:, 2 * H:])
+    return r, z, n, (1.0 - z) * n + z * h_prev
+
+
+def gru_gates_bwd(dh, r, z, n, GH_n, h_prev):
+    """Gate arithmetic of one backward timestep, by the chain rule through
+    gru_gates_fwd, given dh = dL/dh_t (the classifier's part plus the carry
+    from t+1):
+
+        dn = dh (1 - z);  dz = dh (h_prev - n);  dh_dir = dh z
+        dnh = dn (1 - n^2);  dr = dnh GH_n
+        dG_r = dr r (1 - r);  dG_z = dz z (1 - z)
+        dGH = [dG_r | dG_z | dnh r];  dGI = [dG_r | dG_z | dnh]
+
+    Returns (dGH, dGI, dh_dir), float64, unrounded.
+    """
+    dh = np.asarray(dh, dtype=np.float64)
+    dn = dh * (1.0 - z)
+    dz = dh * (h_prev - n)
+    dnh = dn * (1.0 - n * n)
+    dgr = dnh * GH_n * r * (1.0 - r)
+    dgz = dz * z * (1.0 - z)
+    return (np.concatenate([dgr, dgz, dnh * r], axis=1), np.concatenate([dgr, dgz, dnh], axis=1), dh * z)
+
+
 def gru_step(flat, vel, tokens, H: int, V: int, lr: float, momentum: float,
              eps: float = 1e-6, plan: str = "f16", given=None, update: bool = True):
     """One training step; returns a dict of the stored tensors, loss and update.
@@ -100,11 +141,7 @@ def gru_step(flat, vel, tokens, H: int, V: int, lr: float, momentum: float,
             h = np.asarray(given_hs[(t - 1) * Bn:t * Bn], dtype=np.float64)
         h16 = round_fmt(h, lo)
         GH, _ = gemm_epilogue(h16, Pw["W_h"], "NN", bias=P["b_h"], out_fmt=hi)
-        gi = GI[rows]
-        r = _sigmoid(gi[:, :H] + GH[:, :H])
-        z = _sigmoid(gi[:, H:2 * H] + GH[:, H:2 * H])
-        n = np.tanh(gi[:, 2 * H:] + r * GH[:, 2 * H:])
-        hn_ = (1.0 - z) * n + z * h
+        r, z, n, hn_ = gru_gates_fwd(GI[rows], GH, h)
         R[rows] = round_fmt(r, hi); Zg[rows] = round_fmt(z, hi); Nn[rows] = round_fmt(n, hi)
         GHn[rows] = GH[:, 2 * H:]
         hprev16[rows] = h16
@@ -135,16 +172,10 @@ def gru_step(flat, vel, tokens, H: int, V: int, lr: float, momentum: float,
         rows = slice(t * Bn, (t + 1) * Bn)
         r, z, n, ghn = R_u[rows], Z_u[rows], N_u[rows], GHn_u[rows]
         hp = hs_u[(t - 1) * Bn:t * Bn] if t > 0 else np.zeros((Bn, H))
-        dh = dh_out_u[rows] + carry
-        dn = dh * (1.0 - z)
-        dz = dh * (hp - n)
-        dh_dir = round_fmt(dh * z, hi)
-        dnh = dn * (1.0 - n * n)
-        dr = dnh * ghn
-        dgr = dr * r * (1.0 - r)
-        dgz = dz * z * (1.0 - z)
-        dGH[rows] = round_fmt(np.concatenate([dgr, dgz, dnh * r], axis=1), lo)
-        dGI[rows] = round_fmt(np.concatenate([dgr, dgz, dnh], axis=1), lo)
+        dgh, dgi, dh_dir = gru_gates_bwd(dh_out_u[rows] + carry, r, z, n, ghn, hp)
+        dh_dir = round_fmt(dh_dir, hi)
+        dGH[rows] = round_fmt(dgh, lo)
+        dGI[rows] = round_fmt(dgi, lo)
         src = dGH[rows] if gdGH is None else np.asarray(gdGH[rows], dtype=np.float64)
         carry, _ = gemm_epilogue(src, Pw["W_h"], "NT", residual=dh_dir, out_fmt=hi)
     dGH_u, dGI_u = use("dGH", dGH), use("dGI", dGI)

@@ -68,9 +68,17 @@ def test_gemm_rejects_bad_arguments_without_launch(ge):
 def test_other_entry_points_reject_bad_arguments(ge):
     from gemm_epilogue_amd._lib import GE_E_INVALID, RmsnormArgs
     lib = ge.lib
-    assert lib.colsum(None, 4, 4, 4, 9, 1.0, 8, None, 0, None) == GE_E_INVALID
-    assert lib.softmax_xent_fwd_bwd(8, 4, 0, 4, 8, 1.0, 8, 8, None, 0, 0, None, None) == GE_E_INVALID
-    assert lib.softmax_xent_fwd_bwd(8, 4, 10, 9, 8, 1.0, 8, 8, None, 0, 0, None, None) == GE_E_INVALID
+    assert lib.colsum(None, 4, 4, 4, 9, 1.0, 8, 0, None, 0, None) == GE_E_INVALID
+    assert lib.colsum(None, 4, 4, 4, 0, 1.0, 8, 1, None, 0, None) == GE_E_INVALID   # X NULL
+    assert lib.softmax_xent_fwd_bwd(8, 4, 0, 4, 8, 1.0, 8, 8, None, 0, 0, None, None, None) == GE_E_INVALID
+    assert lib.softmax_xent_fwd_bwd(8, 4, 10, 9, 8, 1.0, 8, 8, None, 0, 0, None, 8, None) == GE_E_INVALID
+    assert lib.params_to_lowp(16, 16, 10, 0, None) == GE_E_INVALID         # FP32 is not a low-precision copy
+    assert lib.params_to_lowp(None, 16, 10, 1, None) == GE_E_INVALID
+    assert lib.gru_gates_fwd(16, 16, None, 4, 6, 16, 16, 16, 16, None, None) == GE_E_INVALID   # H % 4
+    assert lib.gru_gates_fwd(16, 16, None, 4, 8, 16, 16, 16, 20, None, None) == GE_E_INVALID   # misaligned h
+    assert lib.gru_gates_bwd(16, None, 16, 16, 16, 16, None, 4, 8, 16, 16, None, None) == GE_E_INVALID
+    assert lib.embedding_grad(16, 8, 0, 16, 10, 20000, 8, 1.0, 16, 8, 16, 1 << 20, None) == GE_E_INVALID
+    assert ge.lib.embedding_grad_workspace_bytes(8192, 256) == (8192 + 257) * 4
     r = RmsnormArgs()
     r.pass_, r.rows, r.D = 5, 4, 8
     assert lib.rmsnorm_fwd_bwd(C.byref(r), None) == GE_E_INVALID

@@ -108,3 +108,53 @@ def test_embedding_gather_and_grad(ge):
     assert_parity(host(g), oracle.round_fmt(0.5 * dE, "f32"), 1e-4, "f32", "dE", cancel=True)
     g2 = ge.embedding_grad(torch.from_numpy(dX).float().cuda(), torch.from_numpy(vi).cuda(), V, 0.5)
     assert torch.equal(g, g2)
+
+
+@pytest.mark.parametrize("B,H", [(3, 68), (64, 1024)])
+def test_gru_gates_entry_points(ge, B, H):
+    """gru_gates_fwd / gru_gates_bwd through the C ABI against the oracle's
+    gate arithmetic, from the same stored inputs (with and without h_prev and
+    carry)."""
+    g = np.random.default_rng(B + H)
+    f32 = lambda a: datagen.representable(a, "f32")
+    GI, GH = f32(g.normal(size=(B, 3 * H))), f32(g.normal(size=(B, 3 * H)))
+    hp, dho, carry = f32(g.normal(size=(B, H))), f32(g.normal(size=(B, H))), f32(g.normal(size=(B, H)))
+    t = lambda a: torch.from_numpy(a).float().cuda()
+    for with_state in (True, False):
+        h16 = torch.empty((B, H), dtype=torch.float16, device="cuda")
+        r, z, n, h, _ = ge.gru_gates_fwd(t(GI), t(GH), t(hp) if with_state else None, h_f16=h16)
+        hp_ref = hp if with_state else np.zeros_like(hp)
+        rr, zr, nr, hr = oracle.gru_gates_fwd(GI, GH, hp_ref)
+        for name, got, ref, cancel in (("r", r, rr, False), ("z", z, zr, False), ("n", n, nr, True),
+                                       ("h", h, hr, True)):
+            assert_parity(host(got), oracle.round_fmt(ref, "f32"), 1e-4, "f32", f"gates fwd {name} B={B}",
+                          cancel=cancel)
+        np.testing.assert_array_equal(host(h16), oracle.round_fmt(host(h), "f16"))
+        # backward from the GPU's stored r, z, n
+        dGH, dGI, dd = ge.gru_gates_bwd(t(dho), t(carry) if with_state else None, r, z, n, t(GH),
+                                        t(hp) if with_state else None)
+        dh = dho + (carry if with_state else 0.0)
+        gH, gI, gd = oracle.gru_gates_bwd(dh, host(r), host(z), host(n), GH[:, 2 * H:], hp_ref)
+        assert_parity(host(dGH), oracle.round_fmt(gH, "f16"), 5e-3, "f16", f"gates dGH B={B}", cancel=True)
+        assert_parity(host(dGI), oracle.round_fmt(gI, "f16"), 5e-3, "f16", f"gates dGI B={B}", cancel=True)
+        assert_parity(host(dd), oracle.round_fmt(gd, "f32"), 1e-4, "f32", f"gates dh_dir B={B}")
+
+
+def test_embedding_grad_zipf_full_size(ge):
+    """8,192 positions (64 x 128) of Zipf(1.1) byte tokens, H = 1024: the most
+    frequent byte holds ~20% of the rows, so its run spans every wave of its
+    block; deterministic and against the oracle's scatter-add."""
+    V, H = 256, 1024
+    tok = datagen.zipf_tokens(64, 128, seed=41)
+    idx = tok.T.reshape(-1).astype(np.int32)
+    dX = datagen.normal((idx.size, H), 1.0, seed=42)
+    tX, ti = torch.from_numpy(dX).float().cuda(), torch.from_numpy(idx).cuda()
+    alpha = 1.0 / idx.size
+    g1 = ge.embedding_grad(tX, ti, V, alpha)
+    g2 = ge.embedding_grad(tX, ti, V, alpha)
+    assert torch.equal(g1, g2)
+    dE = np.zeros((V, H))
+    np.add.at(dE, idx, dX)
+    assert_parity(host(g1), oracle.round_fmt(alpha * dE, "f32"), 1e-4, "f32", "dE zipf", cancel=True)
+    counts = np.bincount(idx, minlength=V)
+    assert counts.max() > 0.15 * idx.size and np.all(host(g1)[counts == 0] == 0.0)

@@ -9,7 +9,7 @@ Two comparisons per checked step:
   only feeds inputs; everything it returns is its own);
 * end-to-end: the step's loss, argmax and update against the oracle's own
   whole step from the same pre-step state, under the loss and argmax rules
-  (loss within 1e-5 relative on the FP32 path; argmax identical unless the
+  (loss within 1e-5 relative on both storage plans; argmax identical unless the
   oracle's top-2 logit gap is below 1e-4).
 """
 import numpy as np
@@ -22,14 +22,11 @@ from parity import TOL_F32, TOL_LOSS, TOL_LOWP, assert_parity, compare
 
 pytestmark = pytest.mark.gpu
 
-# Largest end-to-end relative loss difference accepted for FP16 storage:
-# there the oracle's own step rounds H1, H2 and dZ to FP16 from FP64 values
-# while the GPU rounds FP32 accumulations, so an element at a rounding
-# boundary lands one FP16 ulp (2^-11 relative) apart and the difference
-# propagates into the logits.  The bound is the largest difference observed
-# on the 784-2048-2048-10 steps times a margin; the stage-wise loss (the loss
-# kernel on its own stored input) is held to 1e-5.
-E2E_LOSS_F16 = 2e-4
+# Free-running FP16 trajectories: the GPU and the oracle each round their own
+# FP16 activations, so the two runs part by one-ulp differences that compound
+# over the steps.  Observed over the 50 steps of the 784-2048-2048-10 run: the
+# loss differs by at most 1.1e-3 relative; the bound keeps a margin of ~4x.
+FREE_RUN_LOSS_F16 = 5e-3
 
 
 @pytest.fixture(scope="module")
@@ -89,12 +86,12 @@ def _check_step(tr, dims, X, y, lr, mu, plan, w0, v0, tie_abs, what):
     print(f"{what}: end-to-end loss rel diff {rl:.3e}, argmax differs in {nd_e} rows "
           f"({int(np.count_nonzero(~ok_e))} outside the top-2 gap rule), grads cos {gc['cos']:.9f}, "
           f"mask ties adopted {e2e['mask_ties']}", flush=True)
+    # the loss and argmax rules hold end to end on both storage plans
+    assert rl <= TOL_LOSS, (what, rl)
+    assert np.all(ok_e), (what, nd_e)
     if plan == "f32":
-        assert rl <= TOL_LOSS, (what, rl)
-        assert np.all(ok_e), (what, nd_e)
         assert_parity(host(tr.params), e2e["params"], tol, "f32", f"{what} params end-to-end", cancel=True)
     else:
-        assert rl <= E2E_LOSS_F16, (what, rl)
         assert gc["cos"] > 0.99999, what
     return ref, e2e, rl
 
@@ -190,9 +187,9 @@ def test_cfg2_run_lockstep(ge):
 
 @pytest.mark.timeout(900)
 def test_cfg2_free_running(ge):
-    """The same 50 steps as independent trajectories: final loss and argmax of
-    the final weights on the last batch, reported; the GPU and the oracle
-    each round their own FP16 activations, so only drift is bounded."""
+    """The same 50 steps as independent trajectories: the loss at every step
+    (bounded by the observed drift) and the argmax of the final weights on
+    the last batch (the argmax rule)."""
     dims = datagen.mlp_dims_cfg2()
     B, lr, mu = 4096, 0.05, 0.9
     p0 = datagen.he_uniform_flat(dims)
@@ -214,8 +211,8 @@ def test_cfg2_free_running(ge):
     ok, nd = _argmax_ok(Zg, Zr)
     print(f"784-2048-2048-10 free-running: final loss rel diff {rels[-1]:.3e}, worst {max(rels):.3e}; "
           f"final argmax differs in {nd}/{B} rows ({int(np.count_nonzero(~ok))} outside the gap rule)")
-    assert max(rels) < 1e-2
-    assert np.count_nonzero(~ok) <= B // 1000
+    assert max(rels) <= FREE_RUN_LOSS_F16
+    assert np.all(ok)
 
 
 def test_mlp_hidden_bias_from_dgrad_partials(ge):

@@ -129,3 +129,51 @@ def test_sgd_momentum(ge, pins, n, lowp):
     if lowp:
         # the working copy is the rounding of the GPU's own new FP32 weights
         np.testing.assert_array_equal(host(tl), oracle.round_fmt(host(tw), lowp))
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", [(100, 37), (5000, 1003), (4096, 4096)])
+def test_colsum_accumulate(ge, fmt, shape):
+    """accumulate adds the column sums to what out holds (both the one-pass
+    and the two-pass reduction)."""
+    X = datagen.normal(shape, 1.0, seed=shape[0] + 7, fmt=fmt)
+    base = datagen.normal((shape[1],), 1.0, seed=shape[1] + 8)
+    out = dev(base, "f32")
+    ge.colsum(dev(X, fmt), 0.5, out=out, accumulate=True)
+    ref = oracle.round_fmt(base + oracle.colsum(X, 0.5, out_fmt="f64"), "f32")
+    assert_parity(host(out), ref, TOL_F32 if fmt == "f32" else TOL_LOWP, "f32", f"colsum acc {shape} {fmt}",
+                  cancel=True)
+
+
+def test_softmax_xent_bad_label_count(ge):
+    """Labels outside [0, C) are counted (and give NaN row losses); valid
+    rows are unaffected."""
+    B, C = 300, 10
+    Z = datagen.normal((B, C), 2.0, seed=91, fmt="f32")
+    y = datagen.rng(92, "labels").integers(0, C, size=B).astype(np.int32)
+    y[[3, 77, 150]] = [-1, 10, 1 << 20]
+    bad = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    loss, rl, dZ, am = ge.softmax_xent_fwd_bwd(dev(Z, "f32"), torch.from_numpy(y).cuda(), 1.0 / B,
+                                               bad_label_count=bad)
+    assert int(bad.item()) == 3
+    r = host(rl)
+    assert np.all(np.isnan(r[[3, 77, 150]]))
+    ok = np.ones(B, bool)
+    ok[[3, 77, 150]] = False
+    ref = oracle.softmax_xent(Z[ok], y[ok], 1.0 / B, "f32")
+    assert_parity(r[ok], ref[1], TOL_F32, "f32", "row loss with bad labels present")
+    y2 = np.clip(y, 0, C - 1)
+    ge.softmax_xent_fwd_bwd(dev(Z, "f32"), torch.from_numpy(y2).cuda(), 1.0 / B, bad_label_count=bad)
+    assert int(bad.item()) == 0
+
+
+@pytest.mark.parametrize("n", [1, 7, 203530, 5824522])
+@pytest.mark.parametrize("lowp", ["f16", "bf16"])
+def test_params_to_lowp(ge, n, lowp):
+    """The working copy is the round-to-nearest-even conversion of each value."""
+    w = datagen.normal((n,), 0.05, seed=n + 3)
+    w[:min(n, 4)] = [65520.0, -1e-8, 3.0e38, 0.0][:min(n, 4)]     # overflow, subnormal, bf16 range, zero
+    w = datagen.representable(w, "f32")
+    tl = torch.empty(n, dtype=TD[lowp], device="cuda")
+    ge.params_to_lowp(dev(w, "f32"), tl)
+    np.testing.assert_array_equal(host(tl), oracle.round_fmt(w, lowp))

@@ -337,3 +337,26 @@ def test_gru_given_is_never_returned():
     assert not np.allclose(staged["hs"][Bn:], plain["hs"][Bn:] * 0.5)
     # logits are the classifier of the oracle's own hn of the given hs
     assert not np.allclose(staged["logits"], plain["logits"] + 3.0)
+
+
+def test_gru_gates_bwd_is_the_gradient_of_gates_fwd():
+    """gru_gates_bwd against torch float64 autograd of gru_gates_fwd: with GI,
+    GH and h_prev independent inputs, dGI = dL/dGI, dGH = dL/dGH and
+    dh_dir = dL/dh_prev for L = sum(dh * h)."""
+    from oracle import gru_gates_bwd, gru_gates_fwd
+    g = np.random.default_rng(37)
+    B, H = 5, 7
+    GI, GH = g.normal(size=(B, 3 * H)), g.normal(size=(B, 3 * H))
+    hp, dh = g.normal(size=(B, H)), g.normal(size=(B, H))
+    tGI, tGH, thp = (torch.from_numpy(a.copy()).requires_grad_() for a in (GI, GH, hp))
+    r = torch.sigmoid(tGI[:, :H] + tGH[:, :H])
+    z = torch.sigmoid(tGI[:, H:2 * H] + tGH[:, H:2 * H])
+    n = torch.tanh(tGI[:, 2 * H:] + r * tGH[:, 2 * H:])
+    h = (1 - z) * n + z * thp
+    (h * torch.from_numpy(dh)).sum().backward()
+    rr, zz, nn, hh = gru_gates_fwd(GI, GH, hp)
+    np.testing.assert_allclose(hh, h.detach().numpy(), rtol=1e-14, atol=1e-15)
+    dGH, dGI, dd = gru_gates_bwd(dh, rr, zz, nn, GH[:, 2 * H:], hp)
+    np.testing.assert_allclose(dGI, tGI.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dGH, tGH.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dd, thp.grad.numpy(), rtol=1e-12, atol=1e-14)
