@@ -75,6 +75,8 @@ class GruBuffers(C.Structure):
 SIGNATURES = {
     "ge_abi_version": (i32, []),
     "ge_last_error": (C.c_char_p, []),
+    "ge_launch_count": (i64, []),
+    "ge_clock_probe": (i32, [vp, i32, i32, vp]),
     "gemm_bias_act": (i32, [C.POINTER(GemmArgs), vp]),
     "gemm_workspace_bytes": (i64, [i32, i32, i64, i64, i64, i32]),
     "colsum": (i32, [vp, i64, i64, i64, i32, f32, vp, i32, vp, i64, vp]),

@@ -9,6 +9,7 @@
 namespace ge {
 
 static thread_local char g_err[512] = "";
+static thread_local int64_t g_launches = 0;
 
 void set_error(const char *fmt, ...) {
   va_list ap;
@@ -17,12 +18,14 @@ void set_error(const char *fmt, ...) {
   va_end(ap);
 }
 
+// called after every kernel launch of the library
 int launch_status(const char *what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("%s: launch failed: %s", what, hipGetErrorString(e));
     return GE_E_LAUNCH;
   }
+  ++g_launches;
   return GE_OK;
 }
 
@@ -44,6 +47,7 @@ extern "C" {
 
 int ge_abi_version(void) { return 1; }
 const char *ge_last_error(void) { return g_err; }
+int64_t ge_launch_count(void) { return g_launches; }
 
 int64_t gemm_workspace_bytes(int32_t layout, int32_t ab_type, int64_t M, int64_t N, int64_t K,
                              int32_t split_k) {

@@ -12,6 +12,7 @@ typedef _Float16 half_t;
 typedef __bf16 bf16_t;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef half_t f16x8 __attribute__((ext_vector_type(8)));
 typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
 typedef half_t f16x4 __attribute__((ext_vector_type(4)));

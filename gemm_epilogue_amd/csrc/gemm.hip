@@ -110,6 +110,7 @@ int64_t t256_128(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 127) /
 
 Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   Plan pl;
+  pl.x8 = 0;
   const int bk = ab_type == GE_F32 ? 32 : 64;
   const int nk = (int)((K + bk - 1) / bk);
   const int64_t t256 = ntiles(M, N, 256);
@@ -226,6 +227,16 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart) {
     const int64_t v = 16 / es;
     const bool a_mc = a.layout == GE_TN, b_mc = a.layout != GE_NT;
     gp.clamp = gp.a_vec && gp.b_vec && a.M >= v && a.N >= v && (!a_mc || a.M % v == 0) && (!b_mc || a.N % v == 0);
+  }
+  // the eight-wave 256x256 kernel takes the plan's 256x256 tiles (same tiles
+  // and splits, so the same workspace) when every tile is whole, K is whole
+  // 64-wide k-tiles, the rows are 16-byte aligned and the buffer offsets of
+  // one tile stay below 2^31 bytes
+  if ((a.ab_type == GE_F16 || a.ab_type == GE_BF16) && pl.bm == 256 && pl.bn == 256 && a.M % 256 == 0 &&
+      a.N % 256 == 0 && a.K % 64 == 0 && gp.a_vec && gp.b_vec) {
+    auto span = [&](bool kc, int64_t ld) { return kc ? (255 * ld + a.K) * es : (a.K * ld + 256) * es; };
+    const bool a_kc = a.layout != GE_TN, b_kc = a.layout == GE_NT;
+    if (span(a_kc, a.lda) < ((int64_t)1 << 31) && span(b_kc, a.ldb) < ((int64_t)1 << 31)) pl.x8 = 1;
   }
   gp.tiles_m = pl.tiles_m;
   gp.tiles_n = pl.tiles_n;

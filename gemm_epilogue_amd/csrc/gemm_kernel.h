@@ -613,20 +613,15 @@ __device__ __forceinline__ void block_work(const GemmParams &p, int BM, int BN, 
 }
 
 // ---- epilogue of one BM x BN tile ---------------------------------------------------
-// acc[i][j] holds the 16x16 block (wm0 + 16i, wn0 + 16j) of the tile, lane l
-// owning row l % 16, columns 4(l / 16) .. +3.  The tile is staged through LDS
-// in NPASS passes of BM / NPASS rows.  CSUM: the kernel has the registers
-// to also gather column sums for e.colpart (the 256x256 tiles do not: the
-// four accumulators spill there).
-template <int BM, int BN, int NT, int FM, int FN, int NPASS, int EUQ = 0, bool CSUM = false>
-__device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x4 (&acc)[FM][FN], int tid, int wm0,
-                                           int wn0, int bm0, int bn0, int split) {
-  const int lane = tid & 63;
+// The FP32 tile is staged in LDS in NPASS passes of BM / NPASS rows; `stage`
+// (pass, cs) writes the accumulators of that pass's rows into cs (row-major,
+// CSTRIDE floats per row).  Then all threads walk the staged rows, four
+// consecutive columns per thread, so global stores are whole-row coalesced.
+template <int BM, int BN, int NT, int NPASS, int EUQ, bool CSUM, typename Stage>
+__device__ __forceinline__ void store_tile_staged(const GemmParams &p, char *smem, int tid, int bm0, int bn0,
+                                                  int split, Stage &&stage) {
   constexpr int RP = BM / NPASS;
   constexpr int CSTRIDE = BN + 4;  // floats per staged row (16-byte pad)
-  // The lane owning C[m][n..n+3] of each 16x16 fragment writes it
-  // to the staged tile in LDS; then all threads walk the staged rows, four
-  // consecutive columns per thread, so global stores are whole-row coalesced.
   const EpiParams &e = p.ep;
   const bool fast = (bm0 + BM <= p.M) && (bn0 + BN <= p.N) && e.c_vec && (!e.aux || e.aux_vec) &&
                     (!e.res || e.res_vec) && (!e.pre || e.pre_vec) && (!e.bias || e.bias_vec);
@@ -651,16 +646,7 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x
   const int xin_type = bwd ? e.aux_type : e.res_type;
   float csum[4] = {0.f, 0.f, 0.f, 0.f};
   for (int pass = 0; pass < NPASS; ++pass) {
-    if (wm0 / RP == pass) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wm0 - pass * RP + i * 16 + (lane & 15);
-          const int col = wn0 + j * 16 + (lane >> 4) * 4;
-          *(f32x4 *)(cs + row * CSTRIDE + col) = acc[i][j];
-        }
-    }
+    stage(pass, cs);
     __syncthreads();
     const int m_base = bm0 + pass * RP;
     if (part != nullptr) {
@@ -722,6 +708,31 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x
       *(f32x4 *)(e.colpart + (int64_t)(bm0 / BM) * p.N + bn0 + tid * 4) = t;
     }
   }
+}
+
+// acc[i][j] holds the 16x16 block (wm0 + 16i, wn0 + 16j) of the tile, lane l
+// owning row l % 16, columns 4(l / 16) .. +3; the lane writes its four values
+// to the staged tile.  CSUM: the kernel has the registers to also gather
+// column sums for e.colpart (the 256x256 tiles do not: the four accumulators
+// spill there).
+template <int BM, int BN, int NT, int FM, int FN, int NPASS, int EUQ = 0, bool CSUM = false>
+__device__ __forceinline__ void store_tile(const GemmParams &p, char *smem, f32x4 (&acc)[FM][FN], int tid, int wm0,
+                                           int wn0, int bm0, int bn0, int split) {
+  const int lane = tid & 63;
+  constexpr int RP = BM / NPASS;
+  constexpr int CSTRIDE = BN + 4;
+  store_tile_staged<BM, BN, NT, NPASS, EUQ, CSUM>(p, smem, tid, bm0, bn0, split, [&](int pass, float *cs) {
+    if (wm0 / RP == pass) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int row = wm0 - pass * RP + i * 16 + (lane & 15);
+          const int col = wn0 + j * 16 + (lane >> 4) * 4;
+          *(f32x4 *)(cs + row * CSTRIDE + col) = acc[i][j];
+        }
+    }
+  });
 }
 
 // ---- the kernel ---------------------------------------------------------------
@@ -1120,8 +1131,212 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmParams p) {
   store_tile<BM, BN, NT, FM, FN, NPASS, 4, (BN < 256)>(p, smem, acc, tid, wm0, wn0, bm0, bn0, split);
 }
 
+// ---- 256 x 256 tile on eight waves, 32x32x16 MFMA, LDS filled by DMA ------------------
+// Measured on this GPU: a 16x16x32 MFMA issued back to back from one wave
+// per SIMD reaches about half the matrix rate (about 25 cycles each), the
+// 32x32x16 form about nine tenths; and one wave per SIMD pulls about half the
+// LDS bandwidth that two waves do.  So this kernel runs two waves per SIMD,
+// each owning a 128 x 64 block of the tile (4 x 2 blocks of 32 x 32, 128
+// accumulator registers), on the 32x32x16 MFMA.
+//
+// Operands move from memory to LDS without registers: one buffer load with
+// the LDS flag moves 16 bytes per lane into 1 KB of consecutive LDS, so the
+// tile layout is chosen through the global address each lane loads (the
+// buffer form, not the flat one, so the compiler's LDS-read counters stay
+// exact).  k-tiles are 64 wide (whole 128-byte lines of k-contiguous rows),
+// in two LDS stages of 64 KB: the loads of stage t+1 are issued right after
+// the barrier that opens stage t, so they have one stage of MFMA work to land.
+//   k-contiguous operand: 256 rows x 128 bytes; 16-byte chunk c of row r is
+//     stored at chunk c ^ ((r >> 1) & 7) (a 16-lane fragment read -- 16 rows,
+//     one chunk -- hits 16 distinct bank groups).
+//   m/n-contiguous operand: 64 k-rows x 512 bytes; 32-byte slot s of k-row k
+//     is stored at slot s ^ 2 (k & 3).  Its fragments are read with the
+//     transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+//     lane j receives element j & 3 of the 4 elements read by lanes
+//     (j >> 2) + 4 r, r = 0..3, so lanes reading 4 k-rows x 16 consecutive m
+//     hand each lane 4 k-values of one m (two reads make the 8 of a fragment).
+// Within a stage the fragment reads of the next 16-wide k block are spread
+// between the MFMAs of the current one.
+template <typename T> struct Mfma32;
+template <> struct Mfma32<half_t> {
+  typedef f16x8 V;
+  static __device__ __forceinline__ f32x16 mma(V a, V b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma32<bf16_t> {
+  typedef bf16x8 V;
+  static __device__ __forceinline__ f32x16 mma(V a, V b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int X8_BK = 64;                     // k per stage
+constexpr int X8_TILE = 256 * X8_BK * 2;      // bytes of one operand tile of one stage
+constexpr int X8_STAGE = 2 * X8_TILE;
+constexpr int X8_SMEM = 2 * X8_STAGE > 128 * (256 + 4) * 4 ? 2 * X8_STAGE : 128 * (256 + 4) * 4;
+
+__device__ __forceinline__ int x8_kc_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int x8_mc_swz(int k) { return 2 * (k & 3); }
+
+// Per-lane byte offsets of the two instruction parities of one operand tile
+// (instruction ins covers rows 8 ins .. +7 of a k-contiguous tile, k-rows
+// 2 ins, 2 ins + 1 of an m/n-contiguous one); the rest of the address is
+// uniform and goes in the scalar offset.
+template <bool KC>
+__device__ __forceinline__ void x8_lane_offsets(int64_t ld, int es, int lane, uint32_t (&vo)[2]) {
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    if constexpr (KC) {
+      const int row = par * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ x8_kc_swz(row);
+      vo[par] = (uint32_t)(((lane >> 3) * ld + 8 * c) * es);
+    } else {
+      const int k = par * 2 + (lane >> 5);
+      const int sl = ((lane & 31) >> 1) ^ x8_mc_swz(k);
+      vo[par] = (uint32_t)(((lane >> 5) * ld + 16 * sl + 8 * (lane & 1)) * es);
+    }
+  }
+}
+
+// base points at the tile's first row (k-contiguous) or first column (m/n-contiguous)
+template <bool KC>
+__device__ __forceinline__ void x8_load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int es, int k0, char *lds_tile, int ins,
+                                        const uint32_t (&vo)[2]) {
+  const uint32_t so = KC ? (uint32_t)(((int64_t)(ins * 8) * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * 2) * ld * es);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + ins * 1024), 16, vo[ins & 1], so, 0, 0);
+}
+
+// fragment of the 32x32x16 MFMA: rows r .. r+31 of the operand, k block kb
+// (16 k) of the stage; lane l gets row r + l % 32, k = 16 kb + 8 (l / 32) .. +7
+template <typename V, bool KC>
+__device__ __forceinline__ V x8_frag(const char *tile, int r, int kb, int lane) {
+  if constexpr (KC) {
+    const int row = r + (lane & 31);
+    const int c = (2 * kb + (lane >> 5)) ^ x8_kc_swz(row);
+    return __builtin_bit_cast(V, *(const lds_u32x4 *)(tile + row * 128 + c * 16));
+  } else {
+    const int G = lane >> 4, j = lane & 15;
+    const int k = 16 * kb + 8 * (G >> 1) + (j >> 2);
+    const int slot = (r >> 4) + (G & 1);
+    const char *p0 = tile + k * 512 + ((slot ^ x8_mc_swz(k)) * 32) + 8 * (j & 3);
+    const char *p1 = tile + (k + 4) * 512 + ((slot ^ x8_mc_swz(k + 4)) * 32) + 8 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+    return __builtin_bit_cast(V, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, NT = 512;
+  constexpr bool A_KC = (LAYOUT != GE_TN);
+  constexpr bool B_KC = (LAYOUT == GE_NT);
+  typedef typename Mfma32<T>::V V;
+  __shared__ __attribute__((aligned(1024))) char smem[X8_SMEM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
+  int bm0, bn0, split;
+  block_work(p, BM, BN, bm0, bn0, split);
+  const int nk = p.K / X8_BK;
+  const int kt0 = split * p.ktiles_per_split;
+  const int kt1 = min(nk, kt0 + p.ktiles_per_split);
+  constexpr int es = (int)sizeof(T);
+  // buffer resources based at this tile's rows / columns (offsets stay far below 2^31)
+  const T *Ab = (const T *)p.A + (A_KC ? (int64_t)bm0 * p.lda : (int64_t)bm0);
+  const T *Bb = (const T *)p.B + (B_KC ? (int64_t)bn0 * p.ldb : (int64_t)bn0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)Ab, (short)0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bb, (short)0, 0x7fffffff, 0x00020000);
+  uint32_t voa[2], vob[2];
+  x8_lane_offsets<A_KC>(p.lda, es, lane, voa);
+  x8_lane_offsets<B_KC>(p.ldb, es, lane, vob);
+  // a stage: 32 instructions per operand tile, 4 + 4 per wave
+  auto issue = [&](int t) {
+    char *st = smem + (t & 1) * X8_STAGE;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ins = wave * 4 + u;
+      x8_load<A_KC>(ra, p.lda, es, t * X8_BK, st, ins, voa);
+      x8_load<B_KC>(rb, p.ldb, es, t * X8_BK, st + X8_TILE, ins, vob);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  V fa0[4], fb0[2], fa1[4], fb1[2];
+  auto rd = [&](const char *st, int kb, V(&fa)[4], V(&fb)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = x8_frag<V, B_KC>(st + X8_TILE, wn0 + 32 * j, kb, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = x8_frag<V, A_KC>(st, wm0 + 32 * i, kb, lane);
+  };
+  // the B fragment goes first, so lane l owns C[m = l % 32][n = 8 (e / 4) + 4 (l / 32) + e % 4]
+  auto mma = [&](const V(&fa)[4], const V(&fb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = Mfma32<T>::mma(fb[j], fa[i], acc[i][j]);
+  };
+  constexpr int NR = (A_KC ? 4 : 8) + (B_KC ? 2 : 4);  // LDS read instructions per k block
+  auto phase = [&](const char *st, int kb, V(&fan)[4], V(&fbn)[2], const V(&fac)[4], const V(&fbc)[2],
+                   bool do_mma) {
+    rd(st, kb, fan, fbn);
+    if (do_mma) {
+      mma(fac, fbc);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, (NR + 7) / 8, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (kt0 < kt1) issue(kt0);
+  for (int t = kt0; t < kt1; ++t) {
+    // stage t's loads (the only ones in flight) and the previous stage's LDS reads are done
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    if (t + 1 < kt1) issue(t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const char *st = smem + (t & 1) * X8_STAGE;
+    phase(st, 0, fa0, fb0, fa1, fb1, t > kt0);  // with the MFMAs of the previous stage's last block
+    phase(st, 1, fa1, fb1, fa0, fb0, true);
+    phase(st, 2, fa0, fb0, fa1, fb1, true);
+    phase(st, 3, fa1, fb1, fa0, fb0, true);
+  }
+  if (kt0 < kt1) mma(fa1, fb1);
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();
+  store_tile_staged<BM, BN, NT, 2, 0, false>(p, smem, tid, bm0, bn0, split, [&](int pass, float *cs) {
+    if ((wave >> 2) == pass) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 32 * i + (lane & 31);
+            const int c = wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
+            const f32x16 &v = acc[i][j];
+            *(f32x4 *)(cs + r * (BN + 4) + c) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+          }
+    }
+  });
+}
+
 // ---- launch plan and per-type launchers ---------------------------------------
 struct Plan {
+  int x8;      // the eight-wave 256x256 kernel (k-tiles of 64)
   int bm, bn;  // tile: 256x256, 256x128, 128x128, 64x64, or 128x16 for N <= 16
   int BK;
   int tiles_m, tiles_n, nk, splits, kps;
@@ -1135,6 +1350,12 @@ void launch_t(const Plan &pl, const GemmParams &gp, hipStream_t s) {
   // operand is transposed on its way into LDS (NN, TN), the eight-wave
   // ping-pong kernel when both are k-contiguous (NT) and for short k ranges
   // (split-K blocks of fewer than 16 k-tiles)
+  if constexpr (sizeof(T) == 2) {
+    if (pl.x8) {
+      hipLaunchKernelGGL((gemm_x8_kernel<T, LAYOUT>), grid, dim3(512), 0, s, gp);
+      return;
+    }
+  }
   if (pl.bm == 256 && pl.bn == 128)
     hipLaunchKernelGGL((gemm_w4_kernel<T, LAYOUT, 128>), grid, dim3(256), 0, s, gp);
   else if (pl.bm == 256 && (LAYOUT == GE_NT || pl.kps < 16))

@@ -71,6 +71,17 @@ typedef void *ge_stream_t; /* hipStream_t */
 
 int ge_abi_version(void); /* returns 1 */
 const char *ge_last_error(void);
+/* Number of kernels the calling thread has enqueued through the library so
+ * far (every entry point counts its launches); the difference around a call
+ * is that call's launch count. */
+int64_t ge_launch_count(void);
+/* Shader clock under matrix-core load, for reading measured rates against
+ * the nominal peak: `blocks` blocks of 256 threads each run `iters` rounds of
+ * eight 32x32x16 MFMAs; block b writes ticks[3b] = shader-clock cycles and
+ * ticks[3b + 1] = 100 MHz reference ticks over its chain (ticks[3b + 2] is
+ * 0).  ticks: device int64 [3 * blocks], caller-owned.  GE_E_INVALID for a
+ * NULL buffer or blocks outside [1, 65536]. */
+int ge_clock_probe(int64_t *ticks, int32_t blocks, int32_t iters, ge_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * gemm_bias_act -- C = act(alpha * op(A) op(B) + bias) [+ residual]

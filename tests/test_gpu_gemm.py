@@ -201,3 +201,47 @@ def test_cfg1_4096_sampled(ge, layout):
         cs = host(ge.colsum(out))
         full = host(out)
         assert_parity(cs[cols], oracle.colsum(full[:, cols]), TOL_F32, "f32", "colsum 4096", cancel=True)
+
+
+# ----------- shapes that take the eight-wave 256x256 kernel (32x32x16 MFMA) --
+# whole 256x256 tiles and K a multiple of 64: unsplit when the tiles fill the
+# GPU, split-K (then the finishing pass applies the epilogue) when they do not
+X8 = [(4096, 3072, 256), (3072, 4096, 512), (512, 512, 16384)]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", ["NN", "NT", "TN"])
+@pytest.mark.parametrize("shape", X8, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_x8_tiles_full(ge, fmt, layout, shape):
+    M, N, K = shape
+    print(f"gemm x8 {layout} {fmt} {M}x{N}x{K}", flush=True)
+    sa, sb = shapes_of(M, N, K, layout)
+    A = datagen.normal(sa, 1 / np.sqrt(K), seed=M + N + K, stream="gemm_a", fmt=fmt)
+    B = datagen.normal(sb, 1 / np.sqrt(K), seed=M + N + K, stream="gemm_b", fmt=fmt)
+    bias = datagen.normal((N,), 0.1, seed=K + 1, stream="gemm_bias")
+    tA, tB, tb = dev(A, fmt), dev(B, fmt), dev(bias, "f32")
+    ref, pre_ref = oracle.gemm_epilogue(A, B, layout, 1.0, bias, "relu", out_fmt=fmt, pre_fmt="f32")
+    pre = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    out = ge.gemm_bias_act(tA, tB, layout, bias=tb, act="relu", out_dtype=TD[fmt], pre=pre)
+    assert_parity(host(out), ref, TOL_LOWP, fmt, f"x8 C {layout} {fmt} {shape}", cancel=True)
+    assert_parity(host(pre), pre_ref, TOL_LOWP, "f32", f"x8 pre {layout} {fmt} {shape}", cancel=True)
+
+
+@pytest.mark.parametrize("act", ["lrelu_sq", "relu_mask_bwd", "lrelu_sq_bwd"])
+def test_gemm_x8_epilogue_variants(ge, act):
+    """The fused epilogues on the eight-wave kernel: LeakyReLU^2 with the
+    pre-activation store and a residual, the derivative epilogues on aux."""
+    M, N, K, fmt = 2048, 6144, 512, "bf16"
+    layout = "NT" if act.endswith("bwd") else "NN"
+    sa, sb = shapes_of(M, N, K, layout)
+    A = datagen.normal(sa, 1.0, seed=81, fmt=fmt)
+    B = datagen.normal(sb, 0.05, seed=82, fmt=fmt)
+    aux = datagen.normal((M, N), 1.0, seed=83, fmt=fmt) if act.endswith("bwd") else None
+    res = None if act.endswith("bwd") else datagen.normal((M, N), 1.0, seed=84, fmt=fmt)
+    ref, pre_ref = oracle.gemm_epilogue(A, B, layout, 0.5, None, act, 0.5, aux, res, out_fmt=fmt, pre_fmt=fmt)
+    pre = torch.empty((M, N), dtype=TD[fmt], device="cuda")
+    out = ge.gemm_bias_act(dev(A, fmt), dev(B, fmt), layout, alpha=0.5, act=act, slope=0.5,
+                           aux=None if aux is None else dev(aux, fmt),
+                           residual=None if res is None else dev(res, fmt), pre=pre, out_dtype=TD[fmt])
+    assert_parity(host(out), ref, TOL_LOWP, fmt, f"x8 {act} C", cancel=True)
+    assert_parity(host(pre), pre_ref, TOL_LOWP, fmt, f"x8 {act} pre", cancel=True)
