@@ -1,23 +1,29 @@
 #!/usr/bin/env python3
-"""Throughput of the GEMM-epilogue training step on one MI355X.
+"""Throughput of the GEMM-epilogue training path on one MI355X.
 
-Workload (the step that is timed): one SGD-momentum training step of the
-784-2048-2048-10 ReLU MLP, FP16 storage with FP32 accumulation and FP32
-master weights, batch 4096, lr 0.05, momentum 0.9, on the seeded
-template-plus-noise images; the 50 batches of the run are resident in HBM
-before timing starts.  A step is forward (3 GEMMs with bias/ReLU epilogues),
-softmax cross-entropy forward/backward, the TN weight-gradient GEMMs, column
-sums, the masked NT dgrad GEMMs and one flat momentum update, all in
-libgemm_epilogue.so.
+Headline workload (the timed step): one SGD-momentum training step of the
+784-2048-2048-10 ReLU MLP, FP16 storage with FP32 accumulation and FP32 master
+weights, batch 4096, lr 0.05, momentum 0.9, on the seeded template-plus-noise
+images; the 50 batches of the run are resident in HBM before timing starts.
+A step is the forward GEMMs with bias/ReLU epilogues, the fused output layer
+(logits, softmax cross-entropy, dZ, bias gradient, masked dgrad), the TN
+weight-gradient GEMMs, the masked NT dgrad GEMM and one flat momentum update,
+all in libgemm_epilogue.so.
 
-Printed: one JSON line (stdout) with samples/s, the roofline of the dominant
-kernel (the NN GEMM-epilogue kernel, timed with HIP events on its stream),
-the standalone 4096^3 GEMM-epilogue rates of the three layouts, and the
-oracle's CPU throughput on a bounded sample of the same workload.
+Printed: one JSON line (stdout) with samples/s of that step, the roofline of
+its dominant kernel (timed live with HIP events on its stream), and beside it
+every other configuration of the path -- the 784-256-10 FP32 epoch (with and
+without hipGraph capture), the standalone 4096^3 GEMM-epilogue in three
+layouts, the transformer MLP block forward+backward, the GRU LM step, the
+bandwidth-bound kernels with the Infinity Cache flushed -- each a median with
+its coefficient of variation, the shader clock measured under MFMA load, and
+the oracle's CPU throughput on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -29,19 +35,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16/BF16 MFMA
-# HBM bytes per launch of the roofline kernel (the fwd2 launch below):
-# FETCH_SIZE + WRITE_SIZE counter passes of rocprofv3 over this script, scaled
-# by the counters' reading for a plain copy of known size (--copy-calibration),
-# as listed in profiles/mlp784-2048-2048-10_fp16_b4096_hbm_bytes.md.  Taken on
-# the current kernel; to be re-measured whenever the kernel changes.
-NN_TRAFFIC_BYTES = 101.24e6
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+NOMINAL_GHZ = 2.4          # the clock the dense peak is quoted at
 DIMS = [784, 2048, 2048, 10]
 BATCH, LR, MU, N_BATCHES = 4096, 0.05, 0.9, 50
+
+# HBM bytes per launch of the roofline kernel (the fwd2 launch below), from the
+# FETCH_SIZE and WRITE_SIZE counter passes of rocprofv3 over this script,
+# scaled by the counters' reading for a plain copy of known size (run with
+# --copy-calibration; the factors are listed with the counts under profiles/).
+# Keyed by the SHA-256 of the GEMM kernel sources they were measured on: when
+# the sources change, the figure no longer describes the kernel and `traffic`
+# is reported as null until the counters are taken again.
+TRAFFIC_BY_SOURCE = {
+    # FETCH_SIZE 41,238 KiB x 2.0 + WRITE_SIZE 16,384 KiB x 1.0 per launch
+    "2567cf4956738ce7": 101_232_640,
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_kernel.h", "gemm.hip"):
+        with open(os.path.join(ROOT, "gemm_epilogue_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def mlp_flops_per_sample(dims):
@@ -51,16 +72,48 @@ def mlp_flops_per_sample(dims):
     return 2 * f + dg
 
 
-def event_time_ms(torch, fn, iters):
-    s = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for i in range(iters):
-        fn(i)
-    e1.record(s)
-    e1.synchronize()
-    return e0.elapsed_time(e1)
+def stats(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return float(np.median(xs)), float(xs.std() / xs.mean()) if xs.size > 1 and xs.mean() > 0 else 0.0
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every library call
+    enqueues on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def once(self, fn):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3  # us
+
+    def per_launch(self, fn, reps=10, n=20, warm=3):
+        """Median and CV over `reps` measurements of `n` back-to-back launches
+        each (the host enqueues faster than the kernels run, so no host time
+        enters the interval)."""
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            ts.append(self.once(lambda: [fn() for _ in range(n)]) / n)
+        return stats(ts)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(seconds_target=12.0):
@@ -82,18 +135,32 @@ def cpu_baseline(seconds_target=12.0):
     dt = time.perf_counter() - t0
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] or [1])
-    return {"value": n / dt, "unit": "samples/s", "cores": cores, "kind": "oracle",
+    return {"value": round(n / dt, 1), "unit": "samples/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(), "host_threads": os.cpu_count(),
             "sample": f"{reps} oracle steps of batch 512 of the same 784-2048-2048-10 FP16-storage "
-                      f"workload ({n} samples, {dt:.1f} s, float64 numpy)"}
+                      f"workload ({n} samples, {dt:.1f} s, float64 numpy, {cores} BLAS threads)"}
+
+
+def measure_clock(torch, ge, dev):
+    """Shader clock under MFMA load on all CUs (library probe)."""
+    blocks = 1024
+    ticks = torch.zeros(3 * blocks, dtype=torch.int64, device=dev)
+    lib = ge.lib
+    ge._lib.check(lib.ge_clock_probe(ctypes.c_void_p(ticks.data_ptr()), blocks, 4000,
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)), "ge_clock_probe")
+    torch.cuda.synchronize()
+    t = ticks.view(blocks, 3).cpu().numpy().astype(np.float64)
+    ghz = t[:, 0] / (t[:, 1] / 100e6) / 1e9
+    return round(float(np.median(ghz)), 3)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gemm4096", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="headline step and roofline only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB elementwise copy, the reference dispatch for "
                          "scaling hardware byte counters (FETCH_SIZE / WRITE_SIZE) to bytes")
@@ -109,9 +176,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    tm = Timer(torch)
     K, W = args.steps, args.warmup
 
-    # ---- resident inputs: the run's batches, parameters, buffers ----------
+    # ---- headline: the 784-2048-2048-10 FP16 training step ---------------
     log("generating inputs")
     nb = min(N_BATCHES, max(1, K + W))
     Xs, ys = [], []
@@ -129,17 +197,32 @@ def main():
         step(i)
     torch.cuda.synchronize()
     log("timing steps")
-    ms = event_time_ms(torch, lambda i: step(W + i), K)
+    # K steps bracketed by events (the value), with an event after every step
+    # for the per-step median and CV
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
-    ms_per_step = ms / K
-    samples_per_s = BATCH * K / (ms / 1e3)
+    evs[0].record()
+    for i in range(K):
+        step(W + i)
+        evs[i + 1].record()
+    evs[-1].synchronize()
+    torch.cuda.synchronize()
+    total_ms = evs[0].elapsed_time(evs[-1])
+    per_step_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(K)]
+    ms_per_step = total_ms / K
+    samples_per_s = BATCH * K / (total_ms / 1e3)
     flops_step = mlp_flops_per_sample(DIMS) * BATCH
     loss = float(tr.loss.item())
+    step_med, step_cv = stats(per_step_us)
+    n0 = ge.lib.ge_launch_count()
+    step(0)
+    launches_cfg2 = int(ge.lib.ge_launch_count() - n0)
+    torch.cuda.synchronize()
 
-    # ---- dominant kernel: the 256x128 four-wave GEMM-epilogue kernel, which
-    # runs the step's two 4096x2048x2048 GEMMs (forward fwd2 and the masked
-    # dgrad); its forward launch (H2 = relu(H1 W2 + b2)) is replayed with the
-    # step's own operands on the same stream and timed with HIP events.
+    # ---- roofline: the dominant kernel of the step -------------------------
+    # the 256x128 four-wave GEMM-epilogue kernel runs the step's two
+    # 4096x2048x2048 GEMMs (forward H2 = relu(H1 W2 + b2) and the masked
+    # dgrad); its forward launch is replayed with the step's own operands
     views = tr.workspace_views(BATCH)
     H1, H2 = views["H"]
     lowp = tr.params_lowp
@@ -147,55 +230,19 @@ def main():
     W2 = lowp[o1:o1 + 2048 * 2048].view(2048, 2048)
     b2 = tr.params[o1 + 2048 * 2048:o1 + 2048 * 2048 + 2048]
     f_nn = 2 * BATCH * 2048 * 2048
-
-    def fwd2(i):
-        ge.gemm_bias_act(H1, W2, "NN", bias=b2, act="relu", out=H2)
-
-    for i in range(3):
-        fwd2(i)
-    nn_ms = event_time_ms(torch, fwd2, K) / K
-    nn_tflops = f_nn / (nn_ms / 1e3) / 1e12
+    nn_us, nn_cv = tm.per_launch(lambda: ge.gemm_bias_act(H1, W2, "NN", bias=b2, act="relu", out=H2),
+                                 reps=10, n=20)
+    nn_tflops = f_nn / (nn_us * 1e-6) / 1e12
+    clock = measure_clock(torch, ge, dev)
+    sha = gemm_source_sha()
     roofline = {"bound": "mfma", "achieved": round(nn_tflops, 1), "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(nn_tflops / PEAK_F16_TFLOPS, 4),
-                "traffic": NN_TRAFFIC_BYTES,
+                "traffic": TRAFFIC_BY_SOURCE.get(sha),
                 "kernel": "gemm_w4_kernel<f16, NN, 256x128 tile> (fwd2 of the step, 4096x2048x2048)",
-                "avg_launch_us": round(nn_ms * 1e3, 2)}
-
-    # ---- standalone 4096^3 GEMM + bias + ReLU epilogue, three layouts ------
-    gemm4096 = None
-    if not args.no_gemm4096:
-        gemm4096 = {}
-        M = N = Kd = 4096
-        g = torch.Generator(device="cpu").manual_seed(1)
-        for layout in ("NN", "NT", "TN"):
-            sa = (M, Kd) if layout != "TN" else (Kd, M)
-            sb = (Kd, N) if layout != "NT" else (N, Kd)
-            A = (torch.randn(sa, generator=g) / 64).half().to(dev)
-            Bm = (torch.randn(sb, generator=g) / 64).half().to(dev)
-            bias = (torch.randn(N, generator=g) * 0.1).to(dev)
-            out = torch.empty(M, N, dtype=torch.float16, device=dev)
-            run = lambda i: ge.gemm_bias_act(A, Bm, layout, bias=bias, act="relu", out=out)
-            for i in range(3):
-                run(i)
-            t = event_time_ms(torch, run, 20) / 20
-            tf = 2 * M * N * Kd / (t / 1e3) / 1e12
-            gemm4096[layout] = {"us": round(t * 1e3, 1), "tflops": round(tf, 1),
-                                "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
-            del A, Bm, out
-
-    if args.copy_calibration:
-        # reads 256 MiB and writes 256 MiB; run it twice so one dispatch is warm
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host")
-        cpu = cpu_baseline()
+                "avg_launch_us": round(nn_us, 2), "launch_cv": round(nn_cv, 4),
+                "algorithmic_flop": f_nn, "gemm_source_sha": sha,
+                "measured_clock_ghz": clock,
+                "frac_at_measured_clock": round(nn_tflops / (PEAK_F16_TFLOPS * clock / NOMINAL_GHZ), 4)}
 
     rec = {
         "metric": "train-step samples/s + GEMM-epilogue TFLOP/s (% MFMA peak), 1 MI355X",
@@ -213,13 +260,238 @@ def main():
         "config": {"workload": "mlp-784-2048-2048-10 train step, fp16 storage, fp32 accumulation, "
                                "batch 4096, sgd-momentum lr 0.05 mu 0.9",
                    "global_batch": BATCH, "layers": DIMS, "parallelism": "single-gpu"},
+        "step_us_median": round(step_med, 2),
+        "step_cv": round(step_cv, 4),
         "step_tflops": round(flops_step / (ms_per_step / 1e3) / 1e12, 1),
+        "launches_per_step": launches_cfg2,
         "final_loss": round(loss, 6),
         "roofline": roofline,
-        "gemm_epilogue_4096": gemm4096,
-        "cpu_baseline": cpu,
     }
+    del Xs, ys, tr
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        rec["gemm_epilogue_4096"] = bench_gemm4096(torch, ge, dev, tm)
+        rec["mlp_784_256_10_epoch"] = bench_cfg0(torch, ge, datagen, dev, tm)
+        rec["mlp_block"] = bench_block(torch, ge, datagen, dev, tm)
+        rec["gru_lm_step"] = bench_gru(torch, ge, datagen, dev, tm)
+        rec["bandwidth_kernels"] = bench_bandwidth(torch, ge, datagen, dev, tm)
+
+    if args.copy_calibration:
+        # reads 256 MiB and writes 256 MiB; run it twice so one dispatch is warm
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline()
+    else:
+        rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
+
+
+def bench_gemm4096(torch, ge, dev, tm):
+    """Standalone 4096^3 GEMM + bias + ReLU epilogue, FP16 inputs, three layouts,
+    FP16 and FP32 stores: median of 10 x 20 back-to-back launches."""
+    log("timing the 4096^3 GEMM epilogue")
+    out = {}
+    M = N = Kd = 4096
+    g = torch.Generator(device="cpu").manual_seed(1)
+    for layout in ("NN", "NT", "TN"):
+        sa = (M, Kd) if layout != "TN" else (Kd, M)
+        sb = (Kd, N) if layout != "NT" else (N, Kd)
+        A = (torch.randn(sa, generator=g) / 64).half().to(dev)
+        Bm = (torch.randn(sb, generator=g) / 64).half().to(dev)
+        bias = (torch.randn(N, generator=g) * 0.1).to(dev)
+        r = {}
+        for store, dt in (("f16", torch.float16), ("f32", torch.float32)):
+            C = torch.empty(M, N, dtype=dt, device=dev)
+            us, cv = tm.per_launch(lambda: ge.gemm_bias_act(A, Bm, layout, bias=bias, act="relu", out=C))
+            tf = 2 * M * N * Kd / (us * 1e-6) / 1e12
+            r[store] = {"us": round(us, 1), "cv": round(cv, 4), "tflops": round(tf, 1),
+                        "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+            del C
+        out[layout] = r
+        del A, Bm
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_cfg0(torch, ge, datagen, dev, tm):
+    """784-256-10 FP32, batch 128 (46 batches + 112), lr 0.1, momentum 0.9: one
+    warm-up epoch, then 11 epochs each from the same initial weights and zero
+    velocity, timed per epoch; the same epoch captured once as a hipGraph and
+    replayed 11 times (the capstone's launch-overhead question)."""
+    log("timing the 784-256-10 epoch")
+    dims = datagen.mlp_dims_cfg0()
+    Xall, yall = datagen.template_images(6000, 100, fmt="f32")
+    tX = torch.from_numpy(Xall).float().to(dev)
+    ty = torch.from_numpy(yall).to(dev)
+    p0 = torch.from_numpy(datagen.he_uniform_flat(dims)).float().to(dev)
+    tr = ge.MLPTrainer(dims, 128, torch.float32, params=p0)
+    batches = [(s, min(6000, s + 128)) for s in range(0, 6000, 128)]
+
+    def epoch():
+        for s, e in batches:
+            tr.step(tX[s:e], ty[s:e], 0.1, 0.9)
+
+    def reset():
+        tr.params.copy_(p0)
+        tr.velocity.zero_()
+
+    n0 = ge.lib.ge_launch_count()
+    tr.step(tX[:128], ty[:128], 0.1, 0.9)
+    launches = int(ge.lib.ge_launch_count() - n0)
+    n0 = ge.lib.ge_launch_count()
+    tr.step(tX[5888:], ty[5888:], 0.1, 0.9)
+    launches_last = int(ge.lib.ge_launch_count() - n0)
+    reset()
+    epoch()  # warm-up epoch
+    ts = []
+    for _ in range(11):
+        reset()
+        ts.append(tm.once(epoch))
+    eager_us, eager_cv = stats(ts)
+    # one captured graph holds the whole epoch (47 steps)
+    reset()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        epoch()  # the capture stream's own warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        epoch()
+    reset()
+    graph.replay()
+    torch.cuda.synchronize()
+    gts = []
+    for _ in range(11):
+        reset()
+        gts.append(tm.once(graph.replay))
+    graph_us, graph_cv = stats(gts)
+    # the graph's epoch must land where the eager one does
+    reset()
+    epoch()
+    torch.cuda.synchronize()
+    p_eager = tr.params.clone()
+    reset()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(p_eager, tr.params))
+    del graph, tr
+    return {"samples_per_s": round(6000 / (eager_us * 1e-6), 1), "epoch_us": round(eager_us, 1),
+            "epoch_cv": round(eager_cv, 4), "steps": len(batches),
+            "launches_per_step": launches, "launches_last_step": launches_last,
+            "graph": {"samples_per_s": round(6000 / (graph_us * 1e-6), 1), "epoch_us": round(graph_us, 1),
+                      "epoch_cv": round(graph_cv, 4), "same_params_as_eager": same},
+            "flop_per_epoch": 4.909e9,
+            "note": "median of 11 epochs after a warm-up epoch, each from the initial weights"}
+
+
+def bench_block(torch, ge, datagen, dev, tm):
+    """Transformer MLP block forward+backward, 98,304 x 512, hidden 1536, BF16."""
+    log("timing the MLP block")
+    R, D, F = 98304, 512, 1536
+    x, wu, wd, dy = datagen.block_inputs(R, D, F, seed=3)
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(dev)
+    tx, twu, twd, tdy = t(x), t(wu), t(wd), t(dy)
+    del x, wu, wd, dy
+    o = ge.mlp_block_fwd_bwd(tx, twu, twd, tdy, eps=1e-6, slope=0.5)
+    us, cv = tm.per_launch(lambda: ge.mlp_block_fwd_bwd(tx, twu, twd, tdy, eps=1e-6, slope=0.5, out=o,
+                                                        workspace=o["workspace"]), reps=10, n=3, warm=2)
+    flop = 6 * 2 * R * D * F
+    n0 = ge.lib.ge_launch_count()
+    ge.mlp_block_fwd_bwd(tx, twu, twd, tdy, eps=1e-6, slope=0.5, out=o, workspace=o["workspace"])
+    launches = int(ge.lib.ge_launch_count() - n0)
+    torch.cuda.synchronize()
+    del o, tx, twu, twd, tdy
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(R / (us * 1e-6), 1), "us": round(us, 1), "cv": round(cv, 4),
+            "tflops": round(flop / (us * 1e-6) / 1e12, 1), "frac_of_peak": round(flop / (us * 1e-6) / 1e12 /
+                                                                             PEAK_F16_TFLOPS, 4),
+            "launches": launches, "flop": flop}
+
+
+def bench_gru(torch, ge, datagen, dev, tm):
+    """GRU byte LM training step: V 256, H 1024, batch 64, T 128, lr 0.01, momentum 0.9."""
+    log("timing the GRU LM step")
+    V, H, B, T = 256, 1024, 64, 128
+    import oracle  # noqa: F401  (not used: parameters come from datagen)
+    P = datagen.gru_params(H, V)
+    order = ("E", "W_i", "b_i", "W_h", "b_h", "W_c", "b_c")
+    flat = np.concatenate([np.asarray(P[k], np.float64).ravel() for k in order])
+    tr = ge.GRUTrainer(V, H, B, T, eps=1e-6, params=torch.from_numpy(flat).float().to(dev))
+    tok = torch.from_numpy(datagen.zipf_tokens(B, T + 1, seed=B + T, vocab=V)).to(dev)
+    us, cv = tm.per_launch(lambda: tr.step(tok, 0.01, 0.9), reps=10, n=3, warm=2)
+    n0 = ge.lib.ge_launch_count()
+    tr.step(tok, 0.01, 0.9)
+    launches = int(ge.lib.ge_launch_count() - n0)
+    torch.cuda.synchronize()
+    flop = 6 * 2 * B * T * H * 3 * H + 3 * 2 * B * T * H * V
+    del tr
+    return {"tokens_per_s": round(B * T / (us * 1e-6), 1), "us": round(us, 1), "cv": round(cv, 4),
+            "tflops": round(flop / (us * 1e-6) / 1e12, 1), "launches": launches, "flop": flop,
+            "note": "latency-bound: the recurrence is 2 x 128 dependent small GEMM + gate launches"}
+
+
+def bench_bandwidth(torch, ge, datagen, dev, tm):
+    """HBM-bound kernels.  Cold: back-to-back launches rotating over enough
+    copies of the operands (> 512 MB together) that every launch reads data the
+    256 MB Infinity Cache no longer holds.  Warm: the same operands every launch."""
+    log("timing the bandwidth-bound kernels")
+    out = {}
+
+    def entry(name, nbytes, fns):
+        c_us, c_cv = tm.per_launch(lambda it=iter(range(1 << 30)): fns[next(it) % len(fns)](),
+                                   reps=10, n=4 * len(fns))
+        w_us, w_cv = tm.per_launch(fns[0], reps=10, n=20)
+        out[name] = {"bytes": nbytes, "copies_rotated": len(fns),
+                     "cold": {"us": round(c_us, 2), "cv": round(c_cv, 4), "gbs": round(nbytes / c_us / 1e3, 1),
+                              "frac_of_hbm": round(nbytes / c_us / 1e3 / PEAK_HBM_GBS, 4)},
+                     "warm": {"us": round(w_us, 2), "cv": round(w_cv, 4), "gbs": round(nbytes / w_us / 1e3, 1),
+                              "frac_of_hbm": round(nbytes / w_us / 1e3 / PEAK_HBM_GBS, 4)}}
+
+    def copies(nbytes):
+        return max(2, -(-(600 << 20) // nbytes))
+
+    nb = 4096 * 4096 * 4 + 4096 * 4
+    Xs = [torch.randn(4096, 4096, device=dev) for _ in range(copies(nb))]
+    cs = torch.empty(4096, device=dev)
+    ws = torch.empty(max(1, int(ge.lib.colsum_workspace_bytes(4096, 4096))), dtype=torch.uint8, device=dev)
+    entry("colsum_f32_4096x4096", nb, [lambda X=X: ge.colsum(X, out=cs, workspace=ws) for X in Xs])
+    del Xs
+    R, D = 98304, 512
+    nb = R * D * 2 * 2 + R * 4
+    xs = [torch.randn(R, D, device=dev).to(torch.bfloat16) for _ in range(copies(nb))]
+    ys = [torch.empty_like(x) for x in xs]
+    r = torch.empty(R, device=dev)
+    entry("rmsnorm_fwd_bf16_98304x512", nb,
+          [lambda x=x, y=y: ge.rmsnorm_fwd(x, 1e-6, y=y, r=r) for x, y in zip(xs, ys)])
+    del ys
+    nb = R * D * (2 + 4 + 2 + 2) + R * 4
+    n = copies(nb)
+    dns = [torch.randn(R, D, device=dev) for _ in range(n)]
+    dress = [torch.randn(R, D, device=dev).to(torch.bfloat16) for _ in range(n)]
+    dxs = [torch.empty_like(xs[0]) for _ in range(n)]
+    entry("rmsnorm_bwd_bf16_98304x512", nb,
+          [lambda i=i: ge.rmsnorm_bwd(xs[i % len(xs)], r, dns[i], dres=dress[i], dx=dxs[i]) for i in range(n)])
+    del xs, dns, dress, dxs
+    P = 5824522
+    nb = P * 22
+    n = copies(nb)
+    sets = [(torch.randn(P, device=dev) * 0.05, torch.randn(P, device=dev) * 0.01, torch.zeros(P, device=dev),
+             torch.empty(P, dtype=torch.float16, device=dev)) for _ in range(n)]
+    entry("sgd_momentum_f32_5824522_with_f16_copy", nb,
+          [lambda s=s: ge.sgd_momentum(s[0], s[1], s[2], 0.0, 0.0, s[3]) for s in sets])
+    del sets
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
