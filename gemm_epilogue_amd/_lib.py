@@ -78,6 +78,7 @@ SIGNATURES = {
     "ge_launch_count": (i64, []),
     "ge_clock_probe": (i32, [vp, i32, i32, vp]),
     "gemm_bias_act": (i32, [C.POINTER(GemmArgs), vp]),
+    "gemm_bias_act_noalloc": (i32, [C.POINTER(GemmArgs), vp]),
     "gemm_workspace_bytes": (i64, [i32, i32, i64, i64, i64, i32]),
     "colsum": (i32, [vp, i64, i64, i64, i32, f32, vp, i32, vp, i64, vp]),
     "colsum_workspace_bytes": (i64, [i64, i64]),

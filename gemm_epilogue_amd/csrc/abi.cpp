@@ -87,6 +87,30 @@ int gemm_bias_act(const ge_gemm_args *a, ge_stream_t stream) {
   return gemm_launch(*a, (hipStream_t)stream);
 }
 
+int gemm_bias_act_noalloc(const ge_gemm_args *a, ge_stream_t stream) {
+  CHECK(a != nullptr, "gemm_bias_act_noalloc: args is NULL");
+  CHECK(a->layout >= GE_NN && a->layout <= GE_TN && dtype_ok(a->ab_type) && a->M >= 0 && a->N >= 0 && a->K >= 0 &&
+            a->split_k >= 0 && a->split_k <= 1024,
+        "gemm_bias_act_noalloc: bad layout, type, size or split_k");
+  const int64_t need = gemm_ws_bytes(a->layout, a->ab_type, a->M, a->N, a->K, a->split_k);
+  if (need > scratch_bytes()) {
+    set_error("gemm_bias_act_noalloc: split-K partials need %lld bytes, more than the %lld-byte scratch",
+              (long long)need, (long long)scratch_bytes());
+    return GE_E_WORKSPACE;
+  }
+  ge_gemm_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (need > 0) {
+    void *p = nullptr;
+    const int st = scratch_address(&p);
+    if (st != GE_OK) return st;
+    b.workspace = p;
+    b.workspace_bytes = scratch_bytes();
+  }
+  return gemm_bias_act(&b, stream);
+}
+
 int64_t colsum_workspace_bytes(int64_t M, int64_t N) {
   if (M < 0 || N < 0) return -1;
   return colsum_ws_bytes(M, N);

@@ -109,6 +109,10 @@ int64_t gemm_colsum_bytes(int ab_type, int64_t M, int64_t N, int64_t K);
 // out[n] = alpha * sum over r < rows of part[r][n], rows added in order
 int colsum_rows_launch(const float *part, int64_t rows, int64_t N, float alpha, float *out, hipStream_t st);
 int64_t gemm_ws_bytes(int layout, int ab_type, int64_t M, int64_t N, int64_t K, int split_k);
+// the library's fixed device scratch (gemm_bias_act_noalloc): its address on
+// the current device and its size
+int scratch_address(void **out);
+int64_t scratch_bytes();
 int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int x_type, float alpha,
                   float *out, void *ws, int64_t ws_bytes, hipStream_t s, int accumulate = 0);
 int64_t colsum_ws_bytes(int64_t M, int64_t N);

@@ -2,9 +2,19 @@
 // marshalling into the kernel parameters, and the split-K finishing kernel.
 // The MFMA kernel itself is in gemm_kernel.h, instantiated per operand type
 // in gemm_f16.hip, gemm_bf16.hip and gemm_f32.hip.
+#include <mutex>
+
 #include "gemm_kernel.h"
 
 namespace ge {
+
+// ---- fixed scratch for callers that cannot allocate ------------------------------
+// Split-K partials of gemm_bias_act_noalloc live here instead of in a caller
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends; host code must use the per-device address from
+// hipGetSymbolAddress, never the array's name.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 // Sums split-K partials in split order and applies the epilogue.  The loads
 // of eight splits are issued together (the sum is still taken in split
@@ -290,5 +300,34 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart) {
     hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, gp);
   return launch_status("gemm_bias_act (split-K finish)");
 }
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {nullptr};
+}  // namespace
+
+// device address of this device's scratch array (looked up once per device)
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    set_error("gemm_bias_act_noalloc: no usable current device (%s)", hipGetErrorString(e));
+    return GE_E_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_error("gemm_bias_act_noalloc: hipGetSymbolAddress failed (%s)", hipGetErrorString(e));
+      return GE_E_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GE_OK;
+}
+
+int64_t scratch_bytes() { return kScratchBytes; }
 
 }  // namespace ge

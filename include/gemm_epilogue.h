@@ -141,6 +141,18 @@ typedef struct ge_gemm_args {
 } ge_gemm_args;
 
 int gemm_bias_act(const ge_gemm_args *args, ge_stream_t stream);
+/* gemm_bias_act for callers that cannot allocate (code under stream capture,
+ * serving loops, harnesses that forbid hipMalloc): the same operation and
+ * result bits as gemm_bias_act, but args->workspace is ignored and the split-K
+ * partials live in the library's own fixed device scratch of 64 MiB (one per
+ * GPU, held until the process ends).  No allocation happens in the call.
+ * Returns GE_E_WORKSPACE when the partials would exceed 64 MiB
+ * (gemm_workspace_bytes(...) > 67108864); nothing is enqueued then.  Every
+ * element of the partials is written before it is read, so nothing needs
+ * clearing between calls.  All calls on one GPU share the scratch: calls that
+ * may overlap on one GPU (different streams without ordering, or several
+ * threads) race and must be serialized by the caller. */
+int gemm_bias_act_noalloc(const ge_gemm_args *args, ge_stream_t stream);
 /* bytes of workspace gemm_bias_act needs for this problem with split_k
  * (0 = the automatic choice); 0 when no split is used. */
 int64_t gemm_workspace_bytes(int32_t layout, int32_t ab_type, int64_t M, int64_t N,
