@@ -419,25 +419,30 @@ def bench_block(torch, ge, datagen, dev, tm):
 
 
 def bench_gru(torch, ge, datagen, dev, tm):
-    """GRU byte LM training step: V 256, H 1024, batch 64, T 128, lr 0.01, momentum 0.9."""
+    """GRU byte LM training step: V 256, H 1024, batch 64, T 128, lr 0.01,
+    momentum 0.9; the recurrence as one persistent launch per direction (the
+    default) and as one GEMM and one gate launch per timestep."""
     log("timing the GRU LM step")
     V, H, B, T = 256, 1024, 64, 128
-    import oracle  # noqa: F401  (not used: parameters come from datagen)
     P = datagen.gru_params(H, V)
     order = ("E", "W_i", "b_i", "W_h", "b_h", "W_c", "b_c")
-    flat = np.concatenate([np.asarray(P[k], np.float64).ravel() for k in order])
-    tr = ge.GRUTrainer(V, H, B, T, eps=1e-6, params=torch.from_numpy(flat).float().to(dev))
+    flat = torch.from_numpy(np.concatenate([np.asarray(P[k], np.float64).ravel() for k in order])).float().to(dev)
     tok = torch.from_numpy(datagen.zipf_tokens(B, T + 1, seed=B + T, vocab=V)).to(dev)
-    us, cv = tm.per_launch(lambda: tr.step(tok, 0.01, 0.9), reps=10, n=3, warm=2)
-    n0 = ge.lib.ge_launch_count()
-    tr.step(tok, 0.01, 0.9)
-    launches = int(ge.lib.ge_launch_count() - n0)
-    torch.cuda.synchronize()
     flop = 6 * 2 * B * T * H * 3 * H + 3 * 2 * B * T * H * V
-    del tr
-    return {"tokens_per_s": round(B * T / (us * 1e-6), 1), "us": round(us, 1), "cv": round(cv, 4),
-            "tflops": round(flop / (us * 1e-6) / 1e12, 1), "launches": launches, "flop": flop,
-            "note": "latency-bound: the recurrence is 2 x 128 dependent small GEMM + gate launches"}
+    out = {}
+    for mode in ("persistent", "stepwise"):
+        tr = ge.GRUTrainer(V, H, B, T, eps=1e-6, params=flat, recurrence=mode)
+        us, cv = tm.per_launch(lambda: tr.step(tok, 0.01, 0.9), reps=10, n=3, warm=2)
+        n0 = ge.lib.ge_launch_count()
+        tr.step(tok, 0.01, 0.9)
+        launches = int(ge.lib.ge_launch_count() - n0)
+        torch.cuda.synchronize()
+        out[mode] = {"tokens_per_s": round(B * T / (us * 1e-6), 1), "us": round(us, 1), "cv": round(cv, 4),
+                     "tflops": round(flop / (us * 1e-6) / 1e12, 1), "launches": launches}
+        del tr
+    out["flop"] = flop
+    out["tokens_per_s"] = out["persistent"]["tokens_per_s"]
+    return out
 
 
 def bench_bandwidth(torch, ge, datagen, dev, tm):

@@ -63,7 +63,7 @@ class BlockArgs(C.Structure):
 
 
 class GruDesc(C.Structure):
-    _fields_ = [("V", i64), ("H", i64), ("B", i64), ("T", i64), ("eps", f32)]
+    _fields_ = [("V", i64), ("H", i64), ("B", i64), ("T", i64), ("eps", f32), ("recurrence", i32)]
 
 
 class GruBuffers(C.Structure):

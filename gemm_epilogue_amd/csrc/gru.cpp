@@ -35,6 +35,12 @@ int gru_fwd_launch(const float *GI, const float *GH, const float *hp, int B, int
 int gru_bwd_launch(const float *dh_out, const float *carry, const float *R, const float *Z, const float *N,
                    const float *GH, const float *hp, int B, int H, half_t *dGH, half_t *dGI, float *dh_dir,
                    hipStream_t s);
+bool gru_persist_supported(int64_t B, int64_t H);
+int gru_rec_fwd_launch(const float *GI, const half_t *Wh, const float *bh, int B, int H, int T, float *GH, float *R,
+                       float *Z, float *N, float *HS, half_t *H16, unsigned *sync, hipStream_t s);
+int gru_rec_bwd_launch(const float *dh_out, const half_t *Wh, const float *R, const float *Z, const float *N,
+                       const float *GH, const float *HS, int B, int H, int T, half_t *dGH, half_t *dGI, unsigned *sync,
+                       hipStream_t s);
 }  // namespace ge
 
 using namespace ge;
@@ -60,13 +66,14 @@ inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; 
 
 bool desc_ok(const ge_gru_desc *d) {
   return d && d->V >= 1 && d->V <= 4096 && d->H >= 4 && d->H <= 4096 && d->H % 4 == 0 && d->B >= 1 &&
-         d->T >= 1 && d->B * d->T < (1 << 24) && d->eps >= 0.f;
+         d->T >= 1 && d->B * d->T < (1 << 24) && d->eps >= 0.f && d->recurrence >= GE_GRU_AUTO &&
+         d->recurrence <= GE_GRU_PERSISTENT;
 }
 
 // byte offsets of every workspace region, in GE_GRU_WS_* order
 struct GruLayout {
   int64_t off[GE_GRU_WS_COUNT];
-  int64_t gemm_off, gemm_ws, cs_off, cs_ws, emb_off, emb_ws, total;
+  int64_t gemm_off, gemm_ws, cs_off, cs_ws, emb_off, emb_ws, sync_off, total;
 };
 
 GruLayout layout_of(const ge_gru_desc *d) {
@@ -121,6 +128,8 @@ GruLayout layout_of(const ge_gru_desc *d) {
   L.emb_off = o;
   L.emb_ws = embedding_grad_ws_bytes(NT, V);
   o = align_up(o + L.emb_ws);
+  L.sync_off = o;  // barrier counter and error word of the persistent recurrence
+  o = align_up(o + 8);
   L.total = o;
   return L;
 }
@@ -233,6 +242,13 @@ int gru_lm_train_step(const ge_gru_desc *desc, const ge_gru_buffers *buf, const 
         (long long)L.total);
   hipStream_t s = (hipStream_t)stream;
   const int64_t B = desc->B, T = desc->T, H = desc->H, V = desc->V, NT = B * T, H3 = 3 * H;
+  const bool persist_ok = gru_persist_supported(B, H);
+  if (desc->recurrence == GE_GRU_PERSISTENT && !persist_ok) {
+    set_error("gru_lm_train_step: the persistent recurrence needs B %% 16 == 0, B <= 64, H %% 256 == 0, "
+              "H <= 1536 and cooperative launch");
+    return GE_E_UNSUPPORTED;
+  }
+  const bool persist = persist_ok && desc->recurrence != GE_GRU_STEPWISE;
   char *ws = (char *)buf->workspace;
   auto W = [&](int i) { return (void *)(ws + L.off[i]); };
   int32_t *inp = (int32_t *)W(GE_GRU_WS_INP), *tgt = (int32_t *)W(GE_GRU_WS_TGT);
@@ -266,7 +282,10 @@ int gru_lm_train_step(const ge_gru_desc *desc, const ge_gru_buffers *buf, const 
   g.bias = pm + obi;
   RUN(gemm_launch(g, s));
   // recurrence
-  for (int64_t t = 0; t < T; ++t) {
+  unsigned *sync = (unsigned *)(ws + L.sync_off);
+  if (persist)
+    RUN(gru_rec_fwd_launch(GI, lp + oWh, pm + obh, (int)B, (int)H, (int)T, GH, R, Z, N, HS, H16, sync, s));
+  for (int64_t t = 0; !persist && t < T; ++t) {
     float *GHt = GH + t * B * H3;
     g = gargs(GE_NN, B, H3, H, H16 + t * B * H, H, lp + oWh, H3, GHt, H3, GE_F32, gws, L.gemm_ws);
     g.bias = pm + obh;
@@ -319,7 +338,9 @@ int gru_lm_train_step(const ge_gru_desc *desc, const ge_gru_buffers *buf, const 
   RUN(rmsnorm_launch(rn, s));
   // backpropagation through time
   int cur = 0;  // CARRY[cur] holds the gradient flowing into h_t from t+1
-  for (int64_t t = T - 1; t >= 0; --t) {
+  if (persist)
+    RUN(gru_rec_bwd_launch(DHO, lp + oWh, R, Z, N, GH, HS, (int)B, (int)H, (int)T, dGH, dGI, sync, s));
+  for (int64_t t = T - 1; !persist && t >= 0; --t) {
     float *carry_in = CARRY + cur * B * H, *carry_out = CARRY + (cur ^ 1) * B * H;
     const float *hp = t == 0 ? ZH : HS + (t - 1) * B * H;
     RUN(gru_bwd_launch(DHO + t * B * H, carry_in, R + t * B * H, Z + t * B * H, N + t * B * H, GH + t * B * H3,

@@ -370,10 +370,11 @@ class GRUTrainer:
     working copy that the update keeps in step.
     """
 
-    def __init__(self, V: int, H: int, B: int, T: int, eps: float = 1e-6, device="cuda", params=None):
+    def __init__(self, V: int, H: int, B: int, T: int, eps: float = 1e-6, device="cuda", params=None,
+                 recurrence: str = "auto"):
         from ._lib import GRU_WS, GruBuffers, GruDesc
         self.V, self.H, self.B, self.T = V, H, B, T
-        self.desc = GruDesc(V, H, B, T, eps)
+        self.desc = GruDesc(V, H, B, T, eps, {"auto": 0, "stepwise": 1, "persistent": 2}[recurrence])
         P = gru_param_count(V, H)
         self.P = P
         self.params = torch.zeros(P, dtype=torch.float32, device=device)

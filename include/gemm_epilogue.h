@@ -417,9 +417,21 @@ int gru_gates_bwd(const float *dh_out, const float *carry, const float *r, const
  * each stored tensor lives (GE_GRU_WS_* order; rows time-major, t*B + b).
  * Constraints: V <= 4096, 4 <= H <= 4096, H % 4 == 0.
  * ---------------------------------------------------------------------- */
+/* recurrence: GE_GRU_AUTO picks the persistent kernels when they apply,
+ * GE_GRU_STEPWISE launches a GEMM and a gate kernel per timestep (any size),
+ * GE_GRU_PERSISTENT runs each direction of the recurrence as one cooperative
+ * launch with the block's slice of W_h resident in LDS ([CAT] "Keep state
+ * resident"); it needs B % 16 == 0, B <= 64, H % 256 == 0, H <= 1536 and
+ * cooperative launch support, and returns GE_E_UNSUPPORTED otherwise.  Both
+ * compute the same quantities; only the recurrent GEMMs' summation order
+ * differs. */
+#define GE_GRU_AUTO 0
+#define GE_GRU_STEPWISE 1
+#define GE_GRU_PERSISTENT 2
 typedef struct ge_gru_desc {
   int64_t V, H, B, T;
   float eps;
+  int32_t recurrence; /* GE_GRU_AUTO / GE_GRU_STEPWISE / GE_GRU_PERSISTENT */
 } ge_gru_desc;
 
 typedef struct ge_gru_buffers {

@@ -39,10 +39,10 @@ GIVEN = {"HS": "hs", "R": "R", "Z": "Z", "N": "N", "GH": "GH", "RSTD": "rstd", "
          "DX": "dX"}
 
 
-def _run_and_check(ge, V, H, B, T, lr, mu, params, what, steps=1):
+def _run_and_check(ge, V, H, B, T, lr, mu, params, what, steps=1, recurrence="auto"):
     tok = datagen.zipf_tokens(B, T + 1, seed=B + T, vocab=V)
     flat = datagen.representable(params, "f32")
-    tr = ge.GRUTrainer(V, H, B, T, eps=1e-6, params=torch.from_numpy(flat).float().cuda())
+    tr = ge.GRUTrainer(V, H, B, T, eps=1e-6, params=torch.from_numpy(flat).float().cuda(), recurrence=recurrence)
     vel = np.zeros_like(flat)
     for s in range(steps):
         w0, v0 = host(tr.params), host(tr.velocity)
@@ -74,11 +74,30 @@ def test_gru_small_ragged(ge):
     _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, "small", steps=2)
 
 
-def test_gru_full_size(ge):
-    """Byte vocabulary 256, hidden 1024, batch 64, sequence 128, lr 0.01, momentum 0.9."""
+@pytest.mark.parametrize("recurrence", ["persistent", "stepwise"])
+def test_gru_full_size(ge, recurrence):
+    """Byte vocabulary 256, hidden 1024, batch 64, sequence 128, lr 0.01,
+    momentum 0.9, with the persistent recurrence (W_h resident in LDS, one
+    launch per direction) and with one GEMM and one gate launch per timestep."""
     V, H, B, T = 256, 1024, 64, 128
     p = oracle.gru_flatten(datagen.gru_params(H, V))
-    _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, "cfg4")
+    _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, f"cfg4 {recurrence}", recurrence=recurrence)
+
+
+def test_gru_persistent_small(ge):
+    """The persistent recurrence at the smallest size it takes (B 16, H 256),
+    two steps, lock-step against the oracle."""
+    V, H, B, T = 97, 256, 16, 9
+    p = oracle.gru_flatten(datagen.gru_params(H, V))
+    _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, "persistent small", steps=2, recurrence="persistent")
+
+
+def test_gru_persistent_refuses_unsupported_sizes(ge):
+    from gemm_epilogue_amd._lib import GEError
+    tr = ge.GRUTrainer(100, 68, 3, 7, recurrence="persistent")
+    tok = torch.from_numpy(datagen.zipf_tokens(3, 8, seed=1, vocab=100)).cuda()
+    with pytest.raises(GEError, match="persistent"):
+        tr.step(tok, 0.01, 0.9)
 
 
 def test_gru_zero_weights_ln256(ge):

@@ -241,3 +241,20 @@ def test_mlp_step_deterministic(ge):
             tr.step(torch.from_numpy(X).half().cuda(), torch.from_numpy(y).cuda(), 0.05, 0.9)
         outs.append(tr.params.clone())
     assert torch.equal(outs[0], outs[1])
+
+
+def test_cfg0_launches_per_step_match_the_fused_count(ge, pins):
+    """The 784-256-10 step enqueues the capstone's fused launch count, 10 per
+    step, counted by the library itself: the first forward GEMM (split over
+    K) and its finishing pass, the output GEMM, the two loss kernels, the
+    output layer's bias gradient, its weight gradient, the masked dgrad (whose
+    epilogue also sums the first layer's bias-gradient columns), the first
+    weight gradient and the momentum update."""
+    dims = datagen.mlp_dims_cfg0()
+    X, y = datagen.template_images(128, 3, fmt="f32")
+    p0 = datagen.he_uniform_flat(dims)
+    tr = ge.MLPTrainer(dims, 128, torch.float32, params=torch.from_numpy(p0).float().cuda())
+    tX, ty = torch.from_numpy(X).float().cuda(), torch.from_numpy(y).cuda()
+    n0 = ge.lib.ge_launch_count()
+    tr.step(tX, ty, pins["lr"], pins["momentum"])
+    assert ge.lib.ge_launch_count() - n0 == pins["launches_per_step_fused"]
