@@ -12,54 +12,30 @@
 //                    W_h in LDS -- then the gate arithmetic for its units, the
 //                    stores of r, z, n, h, the FP16 copy of h and GH; then one
 //                    grid-wide barrier (every block needs all of h16_t next).
+//                    A lane's h_{t-1} is its own previous output, kept in
+//                    registers, and the next step's GI is fetched before the
+//                    barrier; all of a lane's h16 loads are issued before the
+//                    first MFMA, so a step waits on memory once.
 //   backward step t: dh = dh_out + carry for its units (the carry is the
 //                    block's own, kept in registers), the gate backward, the
 //                    stores of dGH, dGI; one grid-wide barrier (every block
 //                    needs all of dGH_t); then carry = dh z + dGH_t W_h[u0 +
 //                    j, :]^T, a [B x 3H] x [3H x 16] product with the 16 rows
-//                    of W_h in LDS.
-// Wave w of a block handles batch rows 16 w .. 16 w + 15, so B <= 64 and
-// B % 16 == 0; H % 16 == 0 and the W_h slice (48 H or 48 H bytes) must fit LDS.
+//                    of W_h in LDS, its 3H columns split over four wave groups
+//                    whose partial sums meet in LDS in a fixed order.
+// Wave group w % 4 of a block handles batch rows 16 (w % 4) .. + 15, so B <= 64
+// and B % 16 == 0; H = 256 KB for KB = 1 .. 4, so the W_h slice (48 H or
+// 16 x 3H halves) fits LDS and a lane's loads of one step fit its registers.
 // The gate arithmetic and every stored tensor are those of gru_fwd_kernel /
 // gru_bwd_kernel (seq.hip); only the GEMM's summation order differs.
-//
-// The grid barrier is a counter that every block increments once per barrier
-// and polls until it reaches (barriers so far) x NB.  The launch is
-// cooperative, so all blocks are resident; the poll is still bounded, and a
-// block that gives up sets an error word and every block leaves the kernel.
 #include "common.h"
+#include "persist.h"
 
 namespace ge {
 
 namespace {
 
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8_t;
-
-constexpr int kSpinLimit = 1 << 22;  // polls of about 64 cycles each before giving up
-
-// returns false when the barrier timed out (or another block reported that)
-__device__ __forceinline__ bool grid_barrier(unsigned *count, unsigned target, unsigned *err) {
-  __syncthreads();
-  __shared__ int ok;
-  if (threadIdx.x == 0) {
-    __threadfence();
-    atomicAdd(count, 1u);
-    int good = 1;
-    int spins = 0;
-    while (__hip_atomic_load(count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || ++spins > kSpinLimit) {
-        atomicOr(err, 1u);
-        good = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    __threadfence();
-    ok = good;
-  }
-  __syncthreads();
-  return ok != 0;
-}
 
 __device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + expf(-x)); }
 
@@ -69,17 +45,18 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 15); }
 
 }  // namespace
 
+template <int KB>
 __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__restrict__ GI, const half_t *__restrict__ Wh,
-                                                             const float *__restrict__ bh, int B, int H, int T,
+                                                             const float *__restrict__ bh, int B, int T,
                                                              float *__restrict__ GH, float *__restrict__ R,
                                                              float *__restrict__ Z, float *__restrict__ Nn,
                                                              float *__restrict__ HS, half_t *__restrict__ H16,
                                                              unsigned *__restrict__ sync) {
+  constexpr int H = 256 * KB, H3 = 3 * H;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   half_t *w = (half_t *)smem;  // [48][H]: row c = gate c / 16, unit c % 16; k contiguous, chunks swizzled
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u0 = blockIdx.x * 16;
-  const int H3 = 3 * H, KC = H / 8;  // 16-byte chunks per LDS row
   // W_h columns of this block, transposed into LDS: thread takes (k, gate),
   // reads the 16 units of row k of that gate block and writes them to 16 rows
   for (int p = tid; p < H * 3; p += 256) {
@@ -89,52 +66,51 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int row = g * 16 + u;
-      const int c = k >> 3;
-      w[row * H + swz(row, c) * 8 + (k & 7)] = u < 8 ? a[u] : b[u - 8];
+      w[row * H + swz(row, k >> 3) * 8 + (k & 7)] = u < 8 ? a[u] : b[u - 8];
     }
   }
   const int m = wave * 16 + (lane & 15);  // batch row of this lane
   const int j0 = 4 * (lane >> 4);         // its four units within the block
   const bool live = wave * 16 < B;
-  f32x4 bias[3];
+  f32x4 bias[3], gi[3];
+  f32x4 hp = {0.f, 0.f, 0.f, 0.f};  // h_{t-1} of the lane's (row, units)
 #pragma unroll
   for (int g = 0; g < 3; ++g) bias[g] = *(const f32x4 *)(bh + g * H + u0 + j0);
+  if (live) {
+#pragma unroll
+    for (int g = 0; g < 3; ++g) gi[g] = *(const f32x4 *)(GI + (int64_t)m * H3 + g * H + u0 + j0);
+  }
   __syncthreads();
   for (int t = 0; t < T; ++t) {
     if (live) {
       f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       if (t > 0) {
-        // h16_{t-1} row m, chunks of 32 k; the lane's 8 k values of each chunk
+        // h16_{t-1} row m: the lane's 8 k values of each 32-wide chunk
         const half_t *hrow = H16 + ((int64_t)t * B + m) * H + 8 * (lane >> 4);
-        for (int k0 = 0; k0 < H; k0 += 256) {
-          f16x8 hv[8];
+        f16x8 hv[8 * KB];
 #pragma unroll
-          for (int s = 0; s < 8; ++s) hv[s] = *(const f16x8 *)(hrow + k0 + 32 * s);
+        for (int s = 0; s < 8 * KB; ++s) hv[s] = *(const f16x8 *)(hrow + 32 * s);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const int c = (k0 + 32 * s) / 8 + (lane >> 4);
+        for (int s = 0; s < 8 * KB; ++s) {
+          const int c = 4 * s + (lane >> 4);
 #pragma unroll
-            for (int g = 0; g < 3; ++g) {
-              const int row = g * 16 + (lane & 15);
-              const f16x8 wv = *(const lds_f16x8_t *)(w + row * H + swz(row, c) * 8);
-              acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, hv[s], acc[g], 0, 0, 0);
-            }
+          for (int g = 0; g < 3; ++g) {
+            const int row = g * 16 + (lane & 15);
+            const f16x8 wv = *(const lds_f16x8_t *)(w + row * H + swz(row, c) * 8);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, hv[s], acc[g], 0, 0, 0);
           }
         }
       }
       // lane holds GH[m][g H + u0 + j0 .. +3] (before the bias)
       const int64_t row = (int64_t)t * B + m;
-      const float *gi = GI + row * H3 + u0 + j0;
-      const f32x4 gir = *(const f32x4 *)gi, giz = *(const f32x4 *)(gi + H), gin = *(const f32x4 *)(gi + 2 * H);
-      const f32x4 hp = t > 0 ? *(const f32x4 *)(HS + (row - B) * H + u0 + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
       f32x4 gh[3], r, z, nn, hv;
 #pragma unroll
       for (int g = 0; g < 3; ++g) gh[g] = acc[g] + bias[g];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        r[q] = sigm(gir[q] + gh[0][q]);
-        z[q] = sigm(giz[q] + gh[1][q]);
-        nn[q] = tanhf(gin[q] + r[q] * gh[2][q]);
+        r[q] = sigm(gi[0][q] + gh[0][q]);
+        z[q] = sigm(gi[1][q] + gh[1][q]);
+        nn[q] = tanhf(gi[2][q] + r[q] * gh[2][q]);
         hv[q] = (1.f - z[q]) * nn[q] + z[q] * hp[q];
       }
       const int64_t o = row * H + u0 + j0;
@@ -145,41 +121,58 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
       *(f16x4 *)(H16 + (row + B) * H + u0 + j0) = f16x4{(half_t)hv[0], (half_t)hv[1], (half_t)hv[2], (half_t)hv[3]};
 #pragma unroll
       for (int g = 0; g < 3; ++g) *(f32x4 *)(GH + row * H3 + g * H + u0 + j0) = gh[g];
+      hp = hv;
+      if (t + 1 < T) {
+#pragma unroll
+        for (int g = 0; g < 3; ++g) gi[g] = *(const f32x4 *)(GI + (row + B) * H3 + g * H + u0 + j0);
+      }
     }
     if (t + 1 < T && !grid_barrier(sync, (unsigned)((t + 1) * gridDim.x), sync + 1)) return;
   }
 }
 
-__global__ __launch_bounds__(256, 1) void gru_rec_bwd_kernel(const float *__restrict__ dh_out,
-                                                             const half_t *__restrict__ Wh, const float *__restrict__ R,
-                                                             const float *__restrict__ Z, const float *__restrict__ Nn,
-                                                             const float *__restrict__ GH, const float *__restrict__ HS,
-                                                             int B, int H, int T, half_t *__restrict__ dGH,
-                                                             half_t *__restrict__ dGI, unsigned *__restrict__ sync) {
+template <int KB>
+__global__ __launch_bounds__(1024, 1) void gru_rec_bwd_kernel(const float *__restrict__ dh_out,
+                                                              const half_t *__restrict__ Wh, const float *__restrict__ R,
+                                                              const float *__restrict__ Z, const float *__restrict__ Nn,
+                                                              const float *__restrict__ GH, const float *__restrict__ HS,
+                                                              int B, int T, half_t *__restrict__ dGH,
+                                                              half_t *__restrict__ dGI, unsigned *__restrict__ sync) {
+  constexpr int H = 256 * KB, H3 = 3 * H, KC = H3 / 8;  // 16-byte chunks per W row
+  constexpr int NS = KC / 16;                           // chunk groups (of 4) per wave group
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  half_t *w = (half_t *)smem;  // [16][3H]: rows u0 .. u0 + 15 of W_h, chunks swizzled
+  half_t *w = (half_t *)smem;                      // [16][3H]: rows u0 .. u0 + 15 of W_h, chunks swizzled
+  f32x4 *red = (f32x4 *)(smem + 16 * H3 * 2);      // [3][4][64] partial carries of wave groups 1..3
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave & 3, part = wave >> 2;
   const int u0 = blockIdx.x * 16;
-  const int H3 = 3 * H, KC = H3 / 8;
-  for (int p = tid; p < 16 * KC; p += 256) {
+  for (int p = tid; p < 16 * KC; p += 1024) {
     const int u = p / KC, c = p % KC;
     *(f16x8 *)(w + u * H3 + swz(u, c) * 8) = *(const f16x8 *)(Wh + (int64_t)(u0 + u) * H3 + 8 * c);
   }
-  const int m = wave * 16 + (lane & 15);
+  const int m = rg * 16 + (lane & 15);
   const int j0 = 4 * (lane >> 4);
-  const bool live = wave * 16 < B;
+  const bool live = rg * 16 < B;
+  const bool gate = live && part == 0;  // the waves that run the gate backward and own the carry
   f32x4 carry = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dho, r, z, nn, ghn, h0;
+  auto fetch = [&](int t) {
+    const int64_t row = (int64_t)t * B + m;
+    const int64_t o = row * H + u0 + j0;
+    dho = *(const f32x4 *)(dh_out + o);
+    r = *(const f32x4 *)(R + o);
+    z = *(const f32x4 *)(Z + o);
+    nn = *(const f32x4 *)(Nn + o);
+    ghn = *(const f32x4 *)(GH + row * H3 + 2 * H + u0 + j0);
+    h0 = t > 0 ? *(const f32x4 *)(HS + o - (int64_t)B * H) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  if (gate) fetch(T - 1);
   __syncthreads();
   int nbar = 0;
   for (int t = T - 1; t >= 0; --t) {
     f32x4 dd = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
+    if (gate) {
       const int64_t row = (int64_t)t * B + m;
-      const int64_t o = row * H + u0 + j0;
-      const f32x4 dho = *(const f32x4 *)(dh_out + o);
-      const f32x4 r = *(const f32x4 *)(R + o), z = *(const f32x4 *)(Z + o), nn = *(const f32x4 *)(Nn + o);
-      const f32x4 ghn = *(const f32x4 *)(GH + row * H3 + 2 * H + u0 + j0);
-      const f32x4 h0 = t > 0 ? *(const f32x4 *)(HS + o - (int64_t)B * H) : f32x4{0.f, 0.f, 0.f, 0.f};
       f16x4 gr, gz, gn, gnh;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -201,35 +194,37 @@ __global__ __launch_bounds__(256, 1) void gru_rec_bwd_kernel(const float *__rest
       *(f16x4 *)(dGI + g0) = gr;
       *(f16x4 *)(dGI + g0 + H) = gz;
       *(f16x4 *)(dGI + g0 + 2 * H) = gnh;
+      if (t > 0) fetch(t - 1);
     }
     if (t == 0) break;
     ++nbar;
     if (!grid_barrier(sync, (unsigned)(nbar * gridDim.x), sync + 1)) return;
+    // carry for step t-1: dh z + dGH_t[m, :] W_h[u0 + j, :]^T over the 3H
+    // columns; wave group `part` takes chunks part KC/4 .. (part + 1) KC/4
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (live) {
-      // carry for step t-1: dh z + dGH_t[m, :] W_h[u0 + j, :]^T over the 3H columns
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const half_t *grow = dGH + ((int64_t)t * B + m) * H3 + 8 * (lane >> 4);
-      for (int k0 = 0; k0 < H3; k0 += 256) {
-        f16x8 gv[8];
+      const half_t *grow = dGH + ((int64_t)t * B + m) * H3 + part * (H3 / 4) + 8 * (lane >> 4);
+      f16x8 gv[NS];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) gv[s] = *(const f16x8 *)(grow + k0 + 32 * s);
+      for (int s = 0; s < NS; ++s) gv[s] = *(const f16x8 *)(grow + 32 * s);
+      const int wr = lane & 15;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int c = (k0 + 32 * s) / 8 + (lane >> 4);
-          const int wr = lane & 15;
-          const f16x8 wv = *(const lds_f16x8_t *)(w + wr * H3 + swz(wr, c) * 8);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, gv[s], acc, 0, 0, 0);
-        }
+      for (int s = 0; s < NS; ++s) {
+        const int c = part * (KC / 4) + 4 * s + (lane >> 4);
+        const f16x8 wv = *(const lds_f16x8_t *)(w + wr * H3 + swz(wr, c) * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, gv[s], acc, 0, 0, 0);
       }
-      carry = acc + dd;
+      if (part > 0) red[((part - 1) * 4 + rg) * 64 + lane] = acc;
     }
+    __syncthreads();
+    if (gate) carry = ((acc + red[rg * 64 + lane]) + red[(4 + rg) * 64 + lane]) + red[(8 + rg) * 64 + lane] + dd;
+    // the next writes to red follow the next grid barrier's workgroup barrier
   }
 }
 
 // ---- launchers ------------------------------------------------------------------
 bool gru_persist_supported(int64_t B, int64_t H) {
-  if (B < 1 || B > 64 || B % 16 != 0 || H % 256 != 0 || H < 256) return false;
-  if ((int64_t)48 * H * 2 > 160 * 1024) return false;
+  if (B < 1 || B > 64 || B % 16 != 0 || H % 256 != 0 || H < 256 || H > 1024) return false;
   int dev = 0, coop = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
@@ -238,19 +233,38 @@ bool gru_persist_supported(int64_t B, int64_t H) {
 }
 
 namespace {
-int coop_launch(const void *fn, int blocks, size_t lds, void **args, hipStream_t s, const char *what) {
+
+const void *fwd_kernel(int KB) {
+  switch (KB) {
+    case 1: return (const void *)gru_rec_fwd_kernel<1>;
+    case 2: return (const void *)gru_rec_fwd_kernel<2>;
+    case 3: return (const void *)gru_rec_fwd_kernel<3>;
+    default: return (const void *)gru_rec_fwd_kernel<4>;
+  }
+}
+
+const void *bwd_kernel(int KB) {
+  switch (KB) {
+    case 1: return (const void *)gru_rec_bwd_kernel<1>;
+    case 2: return (const void *)gru_rec_bwd_kernel<2>;
+    case 3: return (const void *)gru_rec_bwd_kernel<3>;
+    default: return (const void *)gru_rec_bwd_kernel<4>;
+  }
+}
+
+int coop_launch(const void *fn, int slot, int blocks, int threads, size_t lds, void **args, hipStream_t s,
+                const char *what) {
   // the dynamic LDS above the default limit has to be granted per kernel
-  static size_t granted[2] = {0, 0};
-  const int which = fn == (const void *)gru_rec_fwd_kernel ? 0 : 1;
-  if (lds > granted[which]) {
+  static size_t granted[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (lds > granted[slot]) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
       (void)hipGetLastError();
       set_error("%s: cannot grant %zu bytes of LDS", what, lds);
       return GE_E_LAUNCH;
     }
-    granted[which] = lds;
+    granted[slot] = lds;
   }
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(256), args, (unsigned)lds, s);
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(threads), args, (unsigned)lds, s);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     set_error("%s: cooperative launch failed: %s", what, hipGetErrorString(e));
@@ -258,6 +272,7 @@ int coop_launch(const void *fn, int blocks, size_t lds, void **args, hipStream_t
   }
   return launch_status(what);
 }
+
 }  // namespace
 
 int fill_zero_launch(void *p, int64_t bytes, hipStream_t s);
@@ -267,8 +282,9 @@ int gru_rec_fwd_launch(const float *GI, const half_t *Wh, const float *bh, int B
                        float *Z, float *N, float *HS, half_t *H16, unsigned *sync, hipStream_t s) {
   int st = fill_zero_launch(sync, 2 * sizeof(unsigned), s);
   if (st != GE_OK) return st;
-  void *args[] = {&GI, &Wh, &bh, &B, &H, &T, &GH, &R, &Z, &N, &HS, &H16, &sync};
-  return coop_launch((const void *)gru_rec_fwd_kernel, H / 16, (size_t)48 * H * 2, args, s, "gru recurrence (forward)");
+  const int KB = H / 256;
+  void *args[] = {&GI, &Wh, &bh, &B, &T, &GH, &R, &Z, &N, &HS, &H16, &sync};
+  return coop_launch(fwd_kernel(KB), KB - 1, H / 16, 256, (size_t)48 * H * 2, args, s, "gru recurrence (forward)");
 }
 
 int gru_rec_bwd_launch(const float *dh_out, const half_t *Wh, const float *R, const float *Z, const float *N,
@@ -276,9 +292,10 @@ int gru_rec_bwd_launch(const float *dh_out, const half_t *Wh, const float *R, co
                        hipStream_t s) {
   int st = fill_zero_launch(sync, 2 * sizeof(unsigned), s);
   if (st != GE_OK) return st;
-  void *args[] = {&dh_out, &Wh, &R, &Z, &N, &GH, &HS, &B, &H, &T, &dGH, &dGI, &sync};
-  return coop_launch((const void *)gru_rec_bwd_kernel, H / 16, (size_t)16 * 3 * H * 2, args, s,
-                     "gru recurrence (backward)");
+  const int KB = H / 256;
+  void *args[] = {&dh_out, &Wh, &R, &Z, &N, &GH, &HS, &B, &T, &dGH, &dGI, &sync};
+  const size_t lds = (size_t)16 * 3 * H * 2 + (size_t)3 * 4 * 64 * 16;
+  return coop_launch(bwd_kernel(KB), 4 + KB - 1, H / 16, 1024, lds, args, s, "gru recurrence (backward)");
 }
 
 }  // namespace ge
