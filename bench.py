@@ -164,6 +164,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB elementwise copy, the reference dispatch for "
                          "scaling hardware byte counters (FETCH_SIZE / WRITE_SIZE) to bytes")
+    ap.add_argument("--only", choices=("gemm4096", "cfg0", "block", "gru", "bandwidth"),
+                    help="time one of the extra workloads alone and print its record (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the path on a single MI355X "
@@ -178,6 +180,15 @@ def main():
     torch.cuda.set_device(dev)
     tm = Timer(torch)
     K, W = args.steps, args.warmup
+
+    if args.only:
+        runs = {"gemm4096": lambda: bench_gemm4096(torch, ge, dev, tm),
+                "cfg0": lambda: bench_cfg0(torch, ge, datagen, dev, tm),
+                "block": lambda: bench_block(torch, ge, datagen, dev, tm),
+                "gru": lambda: bench_gru(torch, ge, datagen, dev, tm),
+                "bandwidth": lambda: bench_bandwidth(torch, ge, datagen, dev, tm)}
+        print(json.dumps({"only": args.only, args.only: runs[args.only]()}), flush=True)
+        return
 
     # ---- headline: the 784-2048-2048-10 FP16 training step ---------------
     log("generating inputs")
@@ -324,74 +335,87 @@ def bench_gemm4096(torch, ge, dev, tm):
 def bench_cfg0(torch, ge, datagen, dev, tm):
     """784-256-10 FP32, batch 128 (46 batches + 112), lr 0.1, momentum 0.9: one
     warm-up epoch, then 11 epochs each from the same initial weights and zero
-    velocity, timed per epoch; the same epoch captured once as a hipGraph and
-    replayed 11 times (the capstone's launch-overhead question)."""
+    velocity, timed per epoch, for the one-launch persistent step (the
+    default plan) and for the launch chain; the chain's epoch is also captured
+    once as a hipGraph and replayed 11 times (the capstone's launch-overhead
+    question)."""
     log("timing the 784-256-10 epoch")
     dims = datagen.mlp_dims_cfg0()
     Xall, yall = datagen.template_images(6000, 100, fmt="f32")
     tX = torch.from_numpy(Xall).float().to(dev)
     ty = torch.from_numpy(yall).to(dev)
     p0 = torch.from_numpy(datagen.he_uniform_flat(dims)).float().to(dev)
-    tr = ge.MLPTrainer(dims, 128, torch.float32, params=p0)
     batches = [(s, min(6000, s + 128)) for s in range(0, 6000, 128)]
 
-    def epoch():
-        for s, e in batches:
-            tr.step(tX[s:e], ty[s:e], 0.1, 0.9)
+    def run(plan, graph_too):
+        tr = ge.MLPTrainer(dims, 128, torch.float32, params=p0, plan=plan)
 
-    def reset():
-        tr.params.copy_(p0)
-        tr.velocity.zero_()
+        def epoch():
+            for s, e in batches:
+                tr.step(tX[s:e], ty[s:e], 0.1, 0.9)
 
-    n0 = ge.lib.ge_launch_count()
-    tr.step(tX[:128], ty[:128], 0.1, 0.9)
-    launches = int(ge.lib.ge_launch_count() - n0)
-    n0 = ge.lib.ge_launch_count()
-    tr.step(tX[5888:], ty[5888:], 0.1, 0.9)
-    launches_last = int(ge.lib.ge_launch_count() - n0)
-    reset()
-    epoch()  # warm-up epoch
-    ts = []
-    for _ in range(11):
+        def reset():
+            tr.params.copy_(p0)
+            tr.velocity.zero_()
+
+        n0 = ge.lib.ge_launch_count()
+        tr.step(tX[:128], ty[:128], 0.1, 0.9)
+        launches = int(ge.lib.ge_launch_count() - n0)
+        n0 = ge.lib.ge_launch_count()
+        tr.step(tX[5888:], ty[5888:], 0.1, 0.9)
+        launches_last = int(ge.lib.ge_launch_count() - n0)
         reset()
-        ts.append(tm.once(epoch))
-    eager_us, eager_cv = stats(ts)
-    # one captured graph holds the whole epoch (47 steps)
-    reset()
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        epoch()  # the capture stream's own warm-up
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
+        epoch()  # warm-up epoch
+        ts = []
+        for _ in range(11):
+            reset()
+            ts.append(tm.once(epoch))
+        eager_us, eager_cv = stats(ts)
+        reset()
         epoch()
-    reset()
-    graph.replay()
-    torch.cuda.synchronize()
-    gts = []
-    for _ in range(11):
-        reset()
-        gts.append(tm.once(graph.replay))
-    graph_us, graph_cv = stats(gts)
-    # the graph's epoch must land where the eager one does
-    reset()
-    epoch()
-    torch.cuda.synchronize()
-    p_eager = tr.params.clone()
-    reset()
-    graph.replay()
-    torch.cuda.synchronize()
-    same = bool(torch.equal(p_eager, tr.params))
-    del graph, tr
-    return {"samples_per_s": round(6000 / (eager_us * 1e-6), 1), "epoch_us": round(eager_us, 1),
-            "epoch_cv": round(eager_cv, 4), "steps": len(batches),
-            "launches_per_step": launches, "launches_last_step": launches_last,
-            "graph": {"samples_per_s": round(6000 / (graph_us * 1e-6), 1), "epoch_us": round(graph_us, 1),
-                      "epoch_cv": round(graph_cv, 4), "same_params_as_eager": same},
-            "flop_per_epoch": 4.909e9,
-            "note": "median of 11 epochs after a warm-up epoch, each from the initial weights"}
+        torch.cuda.synchronize()
+        p_eager = tr.params.clone()
+        out = {"samples_per_s": round(6000 / (eager_us * 1e-6), 1), "epoch_us": round(eager_us, 1),
+               "epoch_cv": round(eager_cv, 4), "us_per_step": round(eager_us / len(batches), 2),
+               "launches_per_step": launches, "launches_last_step": launches_last}
+        if graph_too:
+            # one captured graph holds the whole epoch (47 steps)
+            reset()
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                epoch()  # the capture stream's own warm-up
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph):
+                epoch()
+            reset()
+            graph.replay()
+            torch.cuda.synchronize()
+            gts = []
+            for _ in range(11):
+                reset()
+                gts.append(tm.once(graph.replay))
+            graph_us, graph_cv = stats(gts)
+            # the graph's epoch must land where the eager one does
+            reset()
+            graph.replay()
+            torch.cuda.synchronize()
+            out["graph"] = {"samples_per_s": round(6000 / (graph_us * 1e-6), 1), "epoch_us": round(graph_us, 1),
+                            "epoch_cv": round(graph_cv, 4), "same_params_as_eager": bool(torch.equal(p_eager, tr.params))}
+            del graph
+        del tr
+        return out, p_eager
+
+    pers, p_pers = run("persistent", False)
+    chain, p_chain = run("chain", True)
+    d = (p_pers - p_chain).abs().max().item()
+    res = dict(pers)
+    res.update({"plan": "persistent", "steps": len(batches), "chain": chain,
+                "params_max_abs_diff_persistent_vs_chain": d, "flop_per_epoch": 4.909e9,
+                "note": "median of 11 epochs after a warm-up epoch, each from the initial weights"})
+    return res
 
 
 def bench_block(torch, ge, datagen, dev, tm):

@@ -47,7 +47,7 @@ class RmsnormArgs(C.Structure):
 
 
 class MlpDesc(C.Structure):
-    _fields_ = [("n_layers", i32), ("dims", C.POINTER(i64)), ("storage", i32)]
+    _fields_ = [("n_layers", i32), ("dims", C.POINTER(i64)), ("storage", i32), ("plan", i32)]
 
 
 class MlpBuffers(C.Structure):

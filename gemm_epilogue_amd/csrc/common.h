@@ -125,6 +125,23 @@ int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const fl
 int xent_launch(const float *logits, int64_t B, int64_t C, int64_t ld, const int32_t *labels,
                 float grad_scale, float *loss_mean, float *row_loss, void *dl, int64_t ld_d,
                 int d_type, int32_t *argmax, hipStream_t s, int32_t *bad_label_count = nullptr);
+// persistent one-launch step of a one-hidden-layer FP32 MLP (step_persist.hip)
+struct MlpPersistArgs {
+  const float *X;         // [B x D0]
+  const int32_t *labels;  // [B]
+  float *P, *Gr, *V;      // flat params, grads, velocity: [W1, b1, W2, b2]
+  float *H;               // [B x D1]
+  float *Zl;              // [B x C] logits
+  float *Gz;              // [B x C] dZ, scaled by 1/B
+  float *row_loss;        // [B]
+  float *dH;              // [B x D1]
+  float *loss;            // [1]
+  unsigned *sync;         // [2]: barrier counter, error word (zero at launch)
+  int B, D0, D1, C;
+  float lr, mu;
+};
+bool mlp_persist_supported(int64_t B, int64_t D0, int64_t D1, int64_t C);
+int mlp_persist_launch(const MlpPersistArgs &args, hipStream_t s);
 int to_lowp_launch(const float *w, int64_t n, void *w_lowp, int lowp_type, hipStream_t s);
 int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t s);
 int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D);

@@ -25,7 +25,7 @@ inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; 
 
 struct MlpLayout {
   std::vector<int64_t> h_off;  // H_1..H_{L-1}
-  int64_t z_off, g_off, dh_off[2], loss_off, gemm_ws_off, gemm_ws, cs_ws_off, cs_ws, total;
+  int64_t z_off, g_off, dh_off[2], loss_off, gemm_ws_off, gemm_ws, cs_ws_off, cs_ws, sync_off, total;
   bool head;  // the last layer runs as one fused kernel (mlp_head_kernel)
   int64_t head_off;
 };
@@ -41,7 +41,13 @@ bool desc_ok(const ge_mlp_desc *d) {
   if (!d || d->n_layers < 1 || d->n_layers > 64 || !d->dims) return false;
   for (int i = 0; i <= d->n_layers; ++i)
     if (d->dims[i] < 1 || d->dims[i] > (1 << 20)) return false;
+  if (d->plan < GE_MLP_AUTO || d->plan > GE_MLP_PERSISTENT) return false;
   return d->storage == GE_F32 || d->storage == GE_F16;
+}
+
+// the one-launch step applies to one hidden layer in FP32 of bounded widths
+bool persist_shape(const ge_mlp_desc *d, int64_t B) {
+  return d->n_layers == 2 && d->storage == GE_F32 && mlp_persist_supported(B, d->dims[0], d->dims[1], d->dims[2]);
 }
 
 MlpLayout layout_of(const ge_mlp_desc *d, int64_t B) {
@@ -85,6 +91,8 @@ MlpLayout layout_of(const ge_mlp_desc *d, int64_t B) {
   L.head = use_head(d, B);
   L.head_off = off;
   if (L.head) off = align_up(off + head_ws_bytes(B, d->dims[d->n_layers - 1]));
+  L.sync_off = off;  // barrier counter and error word of the persistent step
+  off = align_up(off + 8);
   L.total = off;
   return L;
 }
@@ -177,6 +185,35 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   const int64_t es = f16 ? 2 : 4;
   char *ws = (char *)buf->workspace;
   const int64_t P = mlp_param_count(nl, d);
+
+  const bool fits = persist_shape(desc, B);
+  if (desc->plan == GE_MLP_PERSISTENT && !fits) {
+    set_error("mlp_train_step: the persistent plan needs one hidden layer in FP32, B <= 128, dims[0] %% 4 == 0 "
+              "and <= 1024, dims[1] %% 64 == 0 and <= 512, dims[2] <= 16 and 128 resident blocks");
+    return GE_E_UNSUPPORTED;
+  }
+  if (fits && desc->plan != GE_MLP_CHAIN) {
+    MlpPersistArgs a;
+    a.X = (const float *)X;
+    a.labels = labels;
+    a.P = buf->params;
+    a.Gr = buf->grads;
+    a.V = buf->velocity;
+    a.H = (float *)(ws + L.h_off[0]);
+    a.Zl = (float *)(ws + L.z_off);
+    a.Gz = (float *)(ws + L.g_off);
+    a.row_loss = (float *)(ws + L.loss_off);
+    a.dH = (float *)(ws + L.dh_off[0]);
+    a.loss = loss_out;
+    a.sync = (unsigned *)(ws + L.sync_off);
+    a.B = (int)B;
+    a.D0 = (int)d[0];
+    a.D1 = (int)d[1];
+    a.C = (int)d[2];
+    a.lr = lr;
+    a.mu = momentum;
+    return mlp_persist_launch(a, s);
+  }
 
   // parameter offsets (elements)
   std::vector<int64_t> w_off(nl + 1), b_off(nl + 1);

@@ -184,14 +184,18 @@ class MLPTrainer:
 
     params / velocity are f32 flat buffers [W1, b1, W2, b2, ...]; with FP16
     storage an FP16 working copy of the parameters is kept beside them.
+    plan: "auto" (the one-launch persistent step where it applies, else the
+    launch chain), "chain" or "persistent".
     """
 
-    def __init__(self, dims, batch: int, storage=torch.float32, device="cuda", params=None):
+    PLANS = {"auto": 0, "chain": 1, "persistent": 2}
+
+    def __init__(self, dims, batch: int, storage=torch.float32, device="cuda", params=None, plan: str = "auto"):
         self.dims = list(dims)
         self.batch = batch
         self.storage = storage
         self._dims_c = (C.c_int64 * len(dims))(*dims)
-        self.desc = MlpDesc(len(dims) - 1, self._dims_c, dtype_code(storage))
+        self.desc = MlpDesc(len(dims) - 1, self._dims_c, dtype_code(storage), self.PLANS[plan])
         P = mlp_param_count(dims)
         self.P = P
         self.params = torch.zeros(P, dtype=torch.float32, device=device)

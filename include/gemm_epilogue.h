@@ -278,10 +278,27 @@ int params_to_lowp(const float *w, void *w_lowp, int64_t n, int32_t lowp_type, g
  * buffers, starting with the first for dH_{L-1} (so after the step dH_{L-1-2k}
  * is in the first and dH_{L-2-2k} in the second).
  * ---------------------------------------------------------------------- */
+/* plan: GE_MLP_AUTO takes the persistent step where it applies, else the
+ * launch chain; GE_MLP_CHAIN enqueues the step as the fixed sequence of
+ * library kernels (any shape); GE_MLP_PERSISTENT runs the whole step as one
+ * launch of 128 resident blocks with two grid-wide barriers ([CAP] "Explain
+ * a different result": the small step is bound by launches) after a tiny
+ * clear of its barrier words, and returns GE_E_UNSUPPORTED unless L = 2,
+ * storage = GE_F32, 1 <= B <= 128, dims[0] % 4 == 0 and <= 1024,
+ * dims[1] % 64 == 0 and <= 512, dims[2] <= 16, and the device holds 128 of
+ * its blocks at once.  X must then be 16-byte aligned (else GE_E_INVALID).
+ * Both plans compute the same step and fill the same workspace slots; their
+ * summation orders differ.  A persistent step whose barrier gave up (it
+ * waits a bounded time) writes a NaN mean loss. */
+#define GE_MLP_AUTO 0
+#define GE_MLP_CHAIN 1
+#define GE_MLP_PERSISTENT 2
+
 typedef struct ge_mlp_desc {
   int32_t n_layers;     /* number of weight layers L >= 1 */
   const int64_t *dims;  /* host [L + 1] widths, dims[0] = input, dims[L] = classes */
   int32_t storage;      /* GE_F32 or GE_F16 */
+  int32_t plan;         /* GE_MLP_AUTO, GE_MLP_CHAIN or GE_MLP_PERSISTENT */
 } ge_mlp_desc;
 
 typedef struct ge_mlp_buffers {

@@ -99,6 +99,8 @@ def test_mlp_workspace_layout(ge):
     assert len(set(offs)) == 6 and all(o % 256 == 0 for o in offs)
     bad = MlpDesc(2, dims, 2)                 # BF16 storage is not a plan of the MLP step
     assert ge.lib.mlp_workspace_bytes(C.byref(bad), 128) == -1
+    assert ge.lib.mlp_workspace_bytes(C.byref(MlpDesc(2, dims, 0, 3)), 128) == -1   # no such step plan
+    assert ge.lib.mlp_workspace_bytes(C.byref(MlpDesc(2, dims, 0, 2)), 128) == n
 
 
 def test_workspace_queries(ge):
