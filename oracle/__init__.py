@@ -28,6 +28,11 @@ Sources, cited by page title and section:
   RMSNorm -> projection -> LeakyReLU^2 -> down projection -> residual ("What
   Worked") and its backward epilogue ("Credits").
 
+``oracle.exact`` holds the bit-exact FP32 definitions of the primitives
+(linear-order sums, one rounding per operation, correctly rounded divide and
+square root) that the library's bit-exact mode reproduces bit for bit; it
+follows "HIP + Vulkan backends -- Phase 3" ("Phase-3 bug hunt").
+
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force on tiny inputs, finite differences or an
 independent library routine; none is "parity unpinned".
