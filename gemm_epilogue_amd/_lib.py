@@ -76,6 +76,8 @@ SIGNATURES = {
     "ge_abi_version": (i32, []),
     "ge_last_error": (C.c_char_p, []),
     "ge_launch_count": (i64, []),
+    "ge_set_bit_exact": (i32, [i32]),
+    "ge_bit_exact": (i32, []),
     "ge_clock_probe": (i32, [vp, i32, i32, vp]),
     "gemm_bias_act": (i32, [C.POINTER(GemmArgs), vp]),
     "gemm_bias_act_noalloc": (i32, [C.POINTER(GemmArgs), vp]),

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm_epilogue.so")
 SOURCES = ["abi.cpp", "train.cpp", "block.cpp", "gru.cpp", "gemm.hip", "gemm_f16.hip", "gemm_bf16.hip",
-           "gemm_f32.hip", "rowops.hip", "seq.hip", "head.hip", "probe.hip", "gru_persist.hip", "step_persist.hip"]
+           "gemm_f32.hip", "rowops.hip", "seq.hip", "head.hip", "probe.hip", "gru_persist.hip", "step_persist.hip",
+           "exact.hip"]
 ARCH = "gfx950"
 
 
@@ -33,9 +34,13 @@ def _flags():
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# the bit-exact kernels: one IEEE rounding per written operation, none fused
+FILE_FLAGS = {"exact.hip": ["-ffp-contract=off"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,5 +1,6 @@
 // extern "C" entry points: host-side validation, then the internal launchers.
 // Nothing is enqueued unless every argument checks out.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -10,6 +11,9 @@ namespace ge {
 
 static thread_local char g_err[512] = "";
 static thread_local int64_t g_launches = 0;
+static std::atomic<int> g_bit_exact{0};
+
+bool bit_exact_on() { return g_bit_exact.load(std::memory_order_relaxed) != 0; }
 
 void set_error(const char *fmt, ...) {
   va_list ap;
@@ -48,6 +52,8 @@ extern "C" {
 int ge_abi_version(void) { return 1; }
 const char *ge_last_error(void) { return g_err; }
 int64_t ge_launch_count(void) { return g_launches; }
+int32_t ge_set_bit_exact(int32_t on) { return g_bit_exact.exchange(on != 0 ? 1 : 0); }
+int32_t ge_bit_exact(void) { return g_bit_exact.load() ? 1 : 0; }
 
 int64_t gemm_workspace_bytes(int32_t layout, int32_t ab_type, int64_t M, int64_t N, int64_t K,
                              int32_t split_k) {
@@ -84,6 +90,7 @@ int gemm_bias_act(const ge_gemm_args *a, ge_stream_t stream) {
   if (a->residual) CHECK(dtype_ok(a->res_type) && a->ld_res >= a->N, "gemm_bias_act: bad residual type / ld");
   if (a->pre) CHECK(dtype_ok(a->pre_type) && a->ld_pre >= a->N, "gemm_bias_act: bad pre type / ld");
   CHECK(a->C != a->A && a->C != a->B, "gemm_bias_act: C aliases an input");
+  if (bit_exact_on()) return gemm_exact_launch(*a, (hipStream_t)stream);
   return gemm_launch(*a, (hipStream_t)stream);
 }
 
@@ -92,7 +99,8 @@ int gemm_bias_act_noalloc(const ge_gemm_args *a, ge_stream_t stream) {
   CHECK(a->layout >= GE_NN && a->layout <= GE_TN && dtype_ok(a->ab_type) && a->M >= 0 && a->N >= 0 && a->K >= 0 &&
             a->split_k >= 0 && a->split_k <= 1024,
         "gemm_bias_act_noalloc: bad layout, type, size or split_k");
-  const int64_t need = gemm_ws_bytes(a->layout, a->ab_type, a->M, a->N, a->K, a->split_k);
+  // the bit-exact kernels keep no partials
+  const int64_t need = bit_exact_on() ? 0 : gemm_ws_bytes(a->layout, a->ab_type, a->M, a->N, a->K, a->split_k);
   if (need > scratch_bytes()) {
     set_error("gemm_bias_act_noalloc: split-K partials need %lld bytes, more than the %lld-byte scratch",
               (long long)need, (long long)scratch_bytes());
@@ -123,6 +131,8 @@ int colsum(const void *X, int64_t M, int64_t N, int64_t ldx, int32_t x_type, flo
   if (N == 0) return GE_OK;
   CHECK(out != nullptr, "colsum: out is NULL");
   if (M > 0) CHECK(X != nullptr && ldx >= N, "colsum: X is NULL or ldx < N");
+  if (bit_exact_on())
+    return colsum_exact_launch(X, M, N, ldx, x_type, alpha, out, accumulate != 0, (hipStream_t)stream);
   return colsum_launch(X, M, N, ldx, x_type, alpha, out, workspace, workspace_bytes, (hipStream_t)stream,
                        accumulate != 0);
 }
@@ -164,6 +174,7 @@ int rmsnorm_fwd_bwd(const ge_rmsnorm_args *a, ge_stream_t stream) {
     CHECK(a->dx != nullptr && dtype_ok(a->dx_type) && a->ld_dx >= a->D, "rmsnorm_fwd_bwd: bad dx");
     if (a->dres) CHECK(dtype_ok(a->dres_type) && a->ld_dres >= a->D, "rmsnorm_fwd_bwd: bad dres");
   }
+  if (bit_exact_on()) return rmsnorm_exact_launch(*a, (hipStream_t)stream);
   return rmsnorm_launch(*a, (hipStream_t)stream);
 }
 
@@ -173,6 +184,7 @@ int sgd_momentum(float *w, const float *g, float *v, float lr, float momentum, i
   if (n == 0) return GE_OK;
   CHECK(w != nullptr && g != nullptr && v != nullptr, "sgd_momentum: w, g or v is NULL");
   if (w_lowp) CHECK(lowp_type == GE_F16 || lowp_type == GE_BF16, "sgd_momentum: lowp_type must be F16 or BF16");
+  if (bit_exact_on()) return sgd_exact_launch(w, g, v, lr, momentum, n, w_lowp, lowp_type, (hipStream_t)stream);
   // without a gradient segment the update only reads g
   return sgd_launch(w, const_cast<float *>(g), v, lr, momentum, n, w_lowp, lowp_type, (hipStream_t)stream);
 }

@@ -142,6 +142,15 @@ struct MlpPersistArgs {
 };
 bool mlp_persist_supported(int64_t B, int64_t D0, int64_t D1, int64_t C);
 int mlp_persist_launch(const MlpPersistArgs &args, hipStream_t s);
+// bit-exact mode (exact.hip): the primitives as fixed sequences of rounded
+// binary32 operations with linear-order sums
+bool bit_exact_on();
+int gemm_exact_launch(const ge_gemm_args &a, hipStream_t s);
+int colsum_exact_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt, float alpha, float *out,
+                        int accumulate, hipStream_t s);
+int sgd_exact_launch(float *w, const float *g, float *v, float lr, float mu, int64_t n, void *wl, int lt,
+                     hipStream_t s);
+int rmsnorm_exact_launch(const ge_rmsnorm_args &a, hipStream_t s);
 int to_lowp_launch(const float *w, int64_t n, void *w_lowp, int lowp_type, hipStream_t s);
 int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t s);
 int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D);

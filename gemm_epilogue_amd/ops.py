@@ -60,6 +60,24 @@ def gemm_workspace_bytes(layout: str, dtype, M, N, K, split_k=0) -> int:
     return int(lib.gemm_workspace_bytes(LAYOUT[layout], dtype_code(dtype), M, N, K, split_k))
 
 
+class bit_exact:
+    """Context manager: the library's bit-exact mode on (or off) inside the
+    block, restored after it.  In the mode gemm_bias_act, colsum, the
+    RMSNorm passes and sgd_momentum compute their documented binary32
+    operation sequences (linear-order sums, one rounding per operation)."""
+
+    def __init__(self, on: bool = True):
+        self.on = on
+
+    def __enter__(self):
+        self.prev = lib.ge_set_bit_exact(1 if self.on else 0)
+        return self
+
+    def __exit__(self, *exc):
+        lib.ge_set_bit_exact(self.prev)
+        return False
+
+
 def gemm_bias_act(A, B, layout: str = "NN", *, out=None, out_dtype=torch.float32, alpha=1.0,
                   bias=None, act: str = "none", slope: float = 0.5, aux=None, residual=None,
                   pre=None, workspace=None, split_k: int = 0):

@@ -32,6 +32,7 @@
  *  [CAP] "Capstone 5: train a network with your CUDA kernels" (Day 100).
  *  [CAT] "The Work Moved Down a Layer" (Cat Chat, Vulkan compute).
  *  [MK]  "Full-Depth MLP Megakernel + Fused Attention Preprocessing".
+ *  [HV3] "HIP + Vulkan backends -- Phase 3 (path to 100%)".
  */
 #ifndef GEMM_EPILOGUE_H
 #define GEMM_EPILOGUE_H
@@ -82,6 +83,36 @@ int64_t ge_launch_count(void);
  * 0).  ticks: device int64 [3 * blocks], caller-owned.  GE_E_INVALID for a
  * NULL buffer or blocks outside [1, 65536]. */
 int ge_clock_probe(int64_t *ticks, int32_t blocks, int32_t iters, ge_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Bit-exact mode -- [HV3] "Phase-3 bug hunt" (linear-order subgroup sum,
+ * correctly rounded divide, refined rsqrt): with the mode on, gemm_bias_act
+ * (and its _noalloc form), colsum, rmsnorm_fwd_bwd and sgd_momentum compute
+ * their outputs as the fixed sequences of IEEE binary32 operations below,
+ * every operation rounded to nearest even, none fused, so a CPU running the
+ * same sequence reproduces every output bit.  Stores convert once with RNE.
+ *   gemm:    acc = +0; for k = 0 .. K-1: acc = acc + a_k * b_k;
+ *            v = alpha * acc; v = v + bias[n]; pre = convert(v);
+ *            RELU: v = v > 0 ? v : +0;  LRELU_SQ: t = v > 0 ? v : s * v, v = t * t;
+ *            RELU_MASK_BWD: v = v * (aux > 0 ? 1 : 0);
+ *            LRELU_SQ_BWD: v = v * (aux > 0 ? 2 * aux : ((2 * s) * s) * aux);
+ *            v = v + residual;  C = convert(v)
+ *   colsum:  t = alpha * (x_0 + x_1 + ... in row order); out = t or out + t
+ *   rmsnorm: FWD ss = sum_j x_j * x_j in j order; r = 1 / sqrt(ss / D + eps);
+ *            y = (x * r) * gamma.  BWD xh = x * r; g = dy * gamma;
+ *            c = (sum_j g * xh in j order) / D; dx = r * (g - xh * c) + dres;
+ *            dgamma[j] = sum over rows in row order of dy * xh (no workspace)
+ *   sgd:     vel = momentum * v - lr * g; v = vel; w = w + vel
+ * Divide and square root are correctly rounded ([HV3] refines the hardware
+ * rsqrt to within one ulp; a correctly rounded sqrt and reciprocal is the
+ * reading a CPU reproduces exactly).  softmax_xent_fwd_bwd and the composite
+ * steps (mlp_train_step, mlp_block_fwd_bwd, gru_lm_train_step) are not
+ * affected: exp and log keep their library rounding.  The mode is one
+ * process-wide switch; one thread per output walks its sum, so it is slow.
+ * ge_set_bit_exact returns the previous setting.
+ * ---------------------------------------------------------------------- */
+int32_t ge_set_bit_exact(int32_t on);
+int32_t ge_bit_exact(void);
 
 /* ------------------------------------------------------------------------
  * gemm_bias_act -- C = act(alpha * op(A) op(B) + bias) [+ residual]

@@ -112,3 +112,16 @@ def test_workspace_queries(ge):
     assert gemm_workspace_bytes("TN", torch.bfloat16, 1536, 512, 98304, split_k=4) == 4 * 1536 * 512 * 4
     assert ge.lib.colsum_workspace_bytes(128, 10) == 0
     assert ge.lib.colsum_workspace_bytes(4096, 4096) > 0
+
+
+def test_bit_exact_switch(ge):
+    assert ge.lib.ge_bit_exact() == 0
+    assert ge.lib.ge_set_bit_exact(1) == 0 and ge.lib.ge_bit_exact() == 1
+    assert ge.lib.ge_set_bit_exact(7) == 1 and ge.lib.ge_bit_exact() == 1   # any nonzero is on
+    assert ge.lib.ge_set_bit_exact(0) == 1 and ge.lib.ge_bit_exact() == 0
+    with ge.bit_exact():
+        assert ge.lib.ge_bit_exact() == 1
+        with ge.bit_exact(False):
+            assert ge.lib.ge_bit_exact() == 0
+        assert ge.lib.ge_bit_exact() == 1
+    assert ge.lib.ge_bit_exact() == 0
