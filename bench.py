@@ -49,7 +49,7 @@ BATCH, LR, MU, N_BATCHES = 4096, 0.05, 0.9, 50
 # is reported as null until the counters are taken again.
 TRAFFIC_BY_SOURCE = {
     # FETCH_SIZE 41,238 KiB x 2.0 + WRITE_SIZE 16,384 KiB x 1.0 per launch
-    "2567cf4956738ce7": 101_232_640,
+    "7a2fce3379316347": 101_232_640,
 }
 
 
