@@ -63,8 +63,16 @@ ge_gemm_args gemm_args(int layout, int t, int64_t M, int64_t N, int64_t K, const
   return a;
 }
 
+// split-K partials of whichever of the six GEMMs needs the most: besides the
+// two weight gradients (K = rows), a short batch makes the up/down
+// projections and the dgrads split their K as well
 int64_t block_ws(int64_t R, int64_t D, int64_t F, int t) {
-  return std::max(gemm_ws_bytes(GE_TN, t, F, D, R, 0), gemm_ws_bytes(GE_TN, t, D, F, R, 0));
+  int64_t w = std::max(gemm_ws_bytes(GE_TN, t, F, D, R, 0), gemm_ws_bytes(GE_TN, t, D, F, R, 0));
+  w = std::max(w, gemm_ws_bytes(GE_NN, t, R, F, D, 0));
+  w = std::max(w, gemm_ws_bytes(GE_NN, t, R, D, F, 0));
+  w = std::max(w, gemm_ws_bytes(GE_NT, t, R, F, D, 0));
+  w = std::max(w, gemm_ws_bytes(GE_NT, t, R, D, F, 0));
+  return w;
 }
 
 }  // namespace
