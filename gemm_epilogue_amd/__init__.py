@@ -8,4 +8,5 @@ from ._lib import GEError, lib  # noqa: F401  (fails loudly when the library is 
 from .ops import (MLPTrainer, colsum, dtype_code, gemm_bias_act, gemm_workspace_bytes,  # noqa: F401
                   mlp_block_fwd_bwd, mlp_param_count, rmsnorm_bwd, rmsnorm_fwd, sgd_momentum,
                   softmax_xent_fwd_bwd, GRUTrainer, embedding_gather, embedding_grad, gru_param_count,
-                  params_to_lowp, gru_gates_fwd, gru_gates_bwd, bit_exact)
+                  params_to_lowp, gru_gates_fwd, gru_gates_bwd, bit_exact,
+                  mlp_block_fwd_fused)

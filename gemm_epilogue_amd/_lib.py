@@ -62,6 +62,12 @@ class BlockArgs(C.Structure):
                 ("dw_up", vp), ("dw_down", vp), ("workspace", vp), ("workspace_bytes", i64)]
 
 
+class BlockFusedArgs(C.Structure):
+    _fields_ = [("rows", i64), ("D", i64), ("F", i64), ("eps", f32), ("slope", f32), ("type", i32),
+                ("x", vp), ("w_up", vp), ("w_down", vp), ("y", vp), ("r", vp), ("n", vp), ("u", vp),
+                ("a", vp), ("workspace", vp), ("workspace_bytes", i64)]
+
+
 class GruDesc(C.Structure):
     _fields_ = [("V", i64), ("H", i64), ("B", i64), ("T", i64), ("eps", f32), ("recurrence", i32)]
 
@@ -78,6 +84,8 @@ SIGNATURES = {
     "ge_launch_count": (i64, []),
     "ge_set_bit_exact": (i32, [i32]),
     "ge_bit_exact": (i32, []),
+    "mlp_block_fused_workspace_bytes": (i64, [i64, i64]),
+    "mlp_block_fwd_fused": (i32, [C.POINTER(BlockFusedArgs), vp]),
     "ge_clock_probe": (i32, [vp, i32, i32, vp]),
     "gemm_bias_act": (i32, [C.POINTER(GemmArgs), vp]),
     "gemm_bias_act_noalloc": (i32, [C.POINTER(GemmArgs), vp]),

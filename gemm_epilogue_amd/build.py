@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm_epilogue.so")
 SOURCES = ["abi.cpp", "train.cpp", "block.cpp", "gru.cpp", "gemm.hip", "gemm_f16.hip", "gemm_bf16.hip",
            "gemm_f32.hip", "rowops.hip", "seq.hip", "head.hip", "probe.hip", "gru_persist.hip", "step_persist.hip",
-           "exact.hip"]
+           "exact.hip", "megakernel.hip"]
 ARCH = "gfx950"
 
 

@@ -189,6 +189,27 @@ int sgd_momentum(float *w, const float *g, float *v, float lr, float momentum, i
   return sgd_launch(w, const_cast<float *>(g), v, lr, momentum, n, w_lowp, lowp_type, (hipStream_t)stream);
 }
 
+int64_t mlp_block_fused_workspace_bytes(int64_t D, int64_t F) {
+  if (D < 0 || F < 0) return -1;
+  return block_fused_ws_bytes(D, F);
+}
+
+int mlp_block_fwd_fused(const ge_block_fused_args *a, ge_stream_t stream) {
+  CHECK(a != nullptr, "mlp_block_fwd_fused: args is NULL");
+  CHECK(a->type == GE_BF16 || a->type == GE_F16, "mlp_block_fwd_fused: type must be BF16 or F16");
+  CHECK(a->rows >= 0 && a->rows < kMaxDim && a->D >= 1 && a->F >= 1 && a->D < kMaxDim && a->F < kMaxDim,
+        "mlp_block_fwd_fused: bad sizes");
+  CHECK(a->eps >= 0.f, "mlp_block_fwd_fused: eps < 0");
+  CHECK(a->w_up != nullptr && a->w_down != nullptr, "mlp_block_fwd_fused: a weight is NULL");
+  if (a->rows > 0) CHECK(a->x != nullptr && a->y != nullptr, "mlp_block_fwd_fused: x or y is NULL");
+  CHECK(a->workspace != nullptr && a->workspace_bytes >= block_fused_ws_bytes(a->D, a->F),
+        "mlp_block_fwd_fused: workspace needs %lld bytes", (long long)block_fused_ws_bytes(a->D, a->F));
+  const uintptr_t al = (uintptr_t)a->x | (uintptr_t)a->y | (uintptr_t)a->w_up | (uintptr_t)a->w_down |
+                       (uintptr_t)a->n | (uintptr_t)a->u | (uintptr_t)a->a | (uintptr_t)a->workspace;
+  CHECK(al % 16 == 0, "mlp_block_fwd_fused: every buffer must be 16-byte aligned");
+  return block_fused_launch(*a, (hipStream_t)stream);
+}
+
 int params_to_lowp(const float *w, void *w_lowp, int64_t n, int32_t lowp_type, ge_stream_t stream) {
   CHECK(n >= 0, "params_to_lowp: n < 0");
   if (n == 0) return GE_OK;

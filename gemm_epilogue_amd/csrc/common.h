@@ -151,6 +151,9 @@ int colsum_exact_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt
 int sgd_exact_launch(float *w, const float *g, float *v, float lr, float mu, int64_t n, void *wl, int lt,
                      hipStream_t s);
 int rmsnorm_exact_launch(const ge_rmsnorm_args &a, hipStream_t s);
+// the block's forward as one kernel (megakernel.hip)
+int64_t block_fused_ws_bytes(int64_t D, int64_t F);
+int block_fused_launch(const ge_block_fused_args &a, hipStream_t s);
 int to_lowp_launch(const float *w, int64_t n, void *w_lowp, int lowp_type, hipStream_t s);
 int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t s);
 int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D);

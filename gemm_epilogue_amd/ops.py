@@ -322,6 +322,25 @@ def mlp_block_fwd_bwd(x, w_up, w_down, dy, *, eps: float = 1e-6, slope: float = 
     return o
 
 
+def mlp_block_fwd_fused(x, w_up, w_down, *, eps: float = 1e-6, slope: float = 0.5, y=None, r=None,
+                        n=None, u=None, a=None, workspace=None):
+    """The block's forward pass as one kernel (see mlp_block_fwd_fused in the
+    header); r, n, u and a are written only when given.  Returns y."""
+    from ._lib import BlockFusedArgs
+    R, D = x.shape
+    F = w_up.shape[1]
+    for tsr in (x, w_up, w_down):
+        if not tsr.is_contiguous():
+            raise ValueError("mlp_block_fwd_fused expects contiguous tensors")
+    y = torch.empty((R, D), dtype=x.dtype, device=x.device) if y is None else y
+    ws = _workspace(int(lib.mlp_block_fused_workspace_bytes(D, F)), x.device, workspace)
+    a = BlockFusedArgs(R, D, F, eps, slope, dtype_code(x.dtype), x.data_ptr(), w_up.data_ptr(), w_down.data_ptr(),
+                       y.data_ptr(), _ptr(r), _ptr(n), _ptr(u), _ptr(a), _ptr(ws),
+                       0 if ws is None else ws.numel() * ws.element_size())
+    check(lib.mlp_block_fwd_fused(C.byref(a), _stream()), "mlp_block_fwd_fused")
+    return y
+
+
 # ------------------------------------------------------- GRU language model ------
 
 def embedding_gather(table, idx, *, out=None, out_dtype=None):

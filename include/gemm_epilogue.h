@@ -388,6 +388,40 @@ int64_t mlp_block_workspace_bytes(int64_t rows, int64_t D, int64_t F, int32_t ty
 int mlp_block_fwd_bwd(const ge_block_args *args, ge_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * mlp_block_fwd_fused -- the block's forward pass as one kernel
+ * [MK] "What Worked": RMSNorm -> up projection -> LeakyReLU^2 -> down
+ * projection -> residual in one kernel, the F-wide intermediate accumulated
+ * in 64-wide chunks on chip and never written to HBM; "What Didn't Work":
+ * that kernel lost to library GEMMs on its GPU, so this is the variant to
+ * measure against the GEMM chain of mlp_block_fwd_bwd, not a replacement.
+ * Same arithmetic and storage as the forward half of mlp_block_fwd_bwd:
+ *   r = 1/sqrt(mean_j x^2 + eps);  n = convert(x r);  u = n W_up (FP32);
+ *   a = convert((u > 0 ? u : slope u)^2);  y = convert(x + a W_down).
+ * type: GE_BF16 or GE_F16, the storage of x, w_up [D x F], w_down [F x D],
+ * y and the optional n, u, a (all device, row-major, contiguous); r: device
+ * f32 [rows] or NULL; n [rows x D] and u [rows x F] are written when not NULL
+ * (what the backward pass consumes), and a [rows x F] too (for checking; the
+ * point of the kernel is that a need not reach HBM).  D must be 512 and F
+ * a positive multiple of 64 (else GE_E_UNSUPPORTED).  workspace: device,
+ * mlp_block_fused_workspace_bytes(D, F) bytes, receives transposed copies of
+ * the two weights (written by a first small kernel of the same call).
+ * ---------------------------------------------------------------------- */
+typedef struct ge_block_fused_args {
+  int64_t rows, D, F;
+  float eps, slope;
+  int32_t type;
+  const void *x, *w_up, *w_down;
+  void *y;
+  float *r;
+  void *n, *u, *a;
+  void *workspace;
+  int64_t workspace_bytes;
+} ge_block_fused_args;
+
+int64_t mlp_block_fused_workspace_bytes(int64_t D, int64_t F);
+int mlp_block_fwd_fused(const ge_block_fused_args *args, ge_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Embedding rows and their gradient (the byte-level recurrent LM).
  * embedding_gather: out[i, :] = table[idx[i], :] for i < n; table [V x H]
  * (type, ld_table), out [n x H] (out_type, ld_out); an index outside [0, V)

@@ -31,10 +31,14 @@ STORED = {"n": "bf16", "u": "bf16", "a": "bf16", "y": "bf16", "du": "bf16", "dx"
           "r": "f32", "dn": "f32", "dW_up": "f32", "dW_down": "f32"}
 
 
-@pytest.mark.parametrize("R,D,F", [(1, 8, 12), (77, 64, 96), (1000, 512, 1536), (4096, 512, 1536)])
-def test_block_stagewise(ge, R, D, F):
-    fmt = "bf16"
-    x, wu, wd, dy = datagen.block_inputs(R, D, F, seed=R)
+@pytest.mark.parametrize("R,D,F,fmt", [(1, 8, 12, "bf16"), (77, 64, 96, "bf16"), (64, 512, 1536, "bf16"),
+                                        (64, 512, 1536, "f16"), (1000, 512, 1536, "bf16"),
+                                        (4096, 512, 1536, "bf16")])
+def test_block_stagewise(ge, R, D, F, fmt):
+    """Every stage against the oracle on the GPU's stored inputs; 64 rows make
+    the projections and dgrads split K too (their partials share the
+    workspace), and one case stores FP16."""
+    x, wu, wd, dy = datagen.block_inputs(R, D, F, seed=R, fmt=fmt)
     o = ge.mlp_block_fwd_bwd(dev(x, fmt), dev(wu, fmt), dev(wd, fmt), dev(dy, fmt), eps=1e-6, slope=0.5)
     torch.cuda.synchronize()
     got = {k: host(o[k]) for k in STORED}
@@ -42,11 +46,12 @@ def test_block_stagewise(ge, R, D, F):
     given = {k: got[k] for k in ("r", "n", "u", "a", "du", "dn")}
     ref = oracle.block_fwd_bwd(x, wu, wd, dy, eps=1e-6, slope=0.5, fmt=fmt, given=given)
     for k, f in STORED.items():
-        assert_parity(got[k], ref[k], TOL_LOWP, f, f"{k} R={R}", cancel=k not in NO_CANCEL)
+        f = fmt if f == "bf16" else f
+        assert_parity(got[k], ref[k], TOL_LOWP, f, f"{k} R={R} {fmt}", cancel=k not in NO_CANCEL)
     # end to end (oracle's own intermediates): reported, cosine-bounded
     e2e = oracle.block_fwd_bwd(x, wu, wd, dy, eps=1e-6, slope=0.5, fmt=fmt)
     for k in ("y", "dx", "dW_up", "dW_down"):
-        c = compare(got[k], e2e[k], TOL_LOWP, STORED[k], cancel=True)
+        c = compare(got[k], e2e[k], TOL_LOWP, fmt if STORED[k] == "bf16" else STORED[k], cancel=True)
         print(f"R={R} {k}: end-to-end cos {c['cos']:.8f}, fails {c['fails']}/{c['n']}")
         assert c["cos"] > 0.9999, k
 
@@ -87,3 +92,58 @@ def test_block_zero_down_projection(ge):
     np.testing.assert_array_equal(host(o["du"]), 0.0)
     np.testing.assert_array_equal(host(o["dW_up"]), 0.0)
     np.testing.assert_array_equal(host(o["dx"]), dy)
+
+
+@pytest.mark.parametrize("R,fmt", [(1000, "bf16"), (64, "f16"), (1, "bf16"), (98304, "bf16")])
+def test_block_fused_forward(ge, R, fmt):
+    """The one-kernel forward (RMSNorm, up, LeakyReLU^2, down, residual; D 512,
+    F 1536), stage-wise: r and n against the oracle's RMSNorm of x, u and a
+    against the oracle's up projection of the GPU's n, y against the oracle's
+    down projection and residual of the GPU's a (y is x plus a sum, checked
+    as such).  At 98,304 rows a sample of rows is checked; the rows are
+    ragged against the 64-row blocks at 1000."""
+    D, F = 512, 1536
+    x, wu, wd, dy = datagen.block_inputs(R, D, F, seed=R + 5, fmt=fmt)
+    tx = dev(x, fmt)
+    r = torch.empty(R, dtype=torch.float32, device="cuda")
+    n = torch.empty((R, D), dtype=TD[fmt], device="cuda")
+    u = torch.empty((R, F), dtype=TD[fmt], device="cuda")
+    a = torch.empty((R, F), dtype=TD[fmt], device="cuda")
+    y = ge.mlp_block_fwd_fused(tx, dev(wu, fmt), dev(wd, fmt), eps=1e-6, slope=0.5, r=r, n=n, u=u, a=a)
+    y_only = ge.mlp_block_fwd_fused(tx, dev(wu, fmt), dev(wd, fmt), eps=1e-6, slope=0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_only)                      # the optional stores change nothing
+    rows = np.arange(R)
+    if R > 4096:
+        rows = np.sort(np.random.default_rng(3).choice(R, 256, replace=False))
+        rows[-1] = R - 1
+    idx = torch.from_numpy(rows).cuda()
+    got = {"r": host(r)[rows], "n": host(n[idx]), "u": host(u[idx]), "a": host(a[idx]), "y": host(y[idx])}
+    ref = oracle.block_fwd_bwd(x[rows], wu, wd, dy[rows], eps=1e-6, slope=0.5, fmt=fmt,
+                               given={"r": got["r"], "n": got["n"], "a": got["a"]})
+    for k in ("r", "n", "u", "a", "y"):
+        f = "f32" if k == "r" else fmt
+        assert_parity(got[k], ref[k], TOL_LOWP, f, f"fused {k} R={R} {fmt}", cancel=k in ("u", "a", "y"))
+    # and against the launch chain's forward on the same inputs
+    if R <= 4096:
+        o = ge.mlp_block_fwd_bwd(tx, dev(wu, fmt), dev(wd, fmt), dev(dy, fmt), eps=1e-6, slope=0.5)
+        torch.cuda.synchronize()
+        # each path rounds a from its own FP32 u (different summation orders),
+        # so a few elements of y differ by an ulp or two where x + a W_down cancels
+        c = compare(host(y), host(o["y"]), TOL_LOWP, fmt, cancel=True)
+        print(f"fused vs chain y R={R}: cos {c['cos']:.10f}, outside the rule {c['fails']}/{c['n']}")
+        assert c["cos"] > 0.99999 and c["fails"] <= 1e-3 * c["n"], c
+
+
+def test_block_fused_refusals(ge):
+    from gemm_epilogue_amd._lib import GEError
+    x = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    wu = torch.zeros((256, 512), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((512, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(GEError, match="D must be 512"):
+        ge.mlp_block_fwd_fused(x, wu, wd)
+    x = torch.zeros((64, 512), dtype=torch.bfloat16, device="cuda")
+    wu = torch.zeros((512, 96), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((96, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(GEError, match="multiple of 64"):
+        ge.mlp_block_fwd_fused(x, wu, wd)
