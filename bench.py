@@ -434,12 +434,37 @@ def bench_block(torch, ge, datagen, dev, tm):
     ge.mlp_block_fwd_bwd(tx, twu, twd, tdy, eps=1e-6, slope=0.5, out=o, workspace=o["workspace"])
     launches = int(ge.lib.ge_launch_count() - n0)
     torch.cuda.synchronize()
-    del o, tx, twu, twd, tdy
+    # the forward alone, A/B: the chain's three launches (RMSNorm; up projection
+    # with the LeakyReLU^2 epilogue and the pre-activation store; down
+    # projection with the residual) against the one-kernel forward, storing y
+    # only and storing what the backward pass reads (r, n, u) as well
+    fflop = 2 * 2 * R * D * F
+    y2 = torch.empty_like(o["y"])
+    fwd = {}
+
+    def chain_fwd():
+        ge.rmsnorm_fwd(tx, 1e-6, y=o["n"], r=o["r"])
+        ge.gemm_bias_act(o["n"], twu, "NN", out=o["a"], act="lrelu_sq", slope=0.5, pre=o["u"])
+        ge.gemm_bias_act(o["a"], twd, "NN", out=o["y"], residual=tx)
+
+    ws = torch.empty(int(ge.lib.mlp_block_fused_workspace_bytes(D, F)), dtype=torch.uint8, device=dev)
+    runs = {"chain": chain_fwd,
+            "fused_y_only": lambda: ge.mlp_block_fwd_fused(tx, twu, twd, y=y2, workspace=ws),
+            "fused_with_r_n_u": lambda: ge.mlp_block_fwd_fused(tx, twu, twd, y=y2, r=o["r"], n=o["n"], u=o["u"],
+                                                               workspace=ws)}
+    for name, fn in runs.items():
+        fus, fcv = tm.per_launch(fn, reps=10, n=5, warm=2)
+        fwd[name] = {"us": round(fus, 1), "cv": round(fcv, 4), "tokens_per_s": round(R / (fus * 1e-6), 1),
+                     "tflops": round(fflop / (fus * 1e-6) / 1e12, 1)}
+    torch.cuda.synchronize()
+    fwd["fused_vs_chain_y_cos"] = float(torch.nn.functional.cosine_similarity(
+        y2.float().flatten(), o["y"].float().flatten(), dim=0))
+    del o, tx, twu, twd, tdy, y2, ws
     torch.cuda.empty_cache()
     return {"tokens_per_s": round(R / (us * 1e-6), 1), "us": round(us, 1), "cv": round(cv, 4),
             "tflops": round(flop / (us * 1e-6) / 1e12, 1), "frac_of_peak": round(flop / (us * 1e-6) / 1e12 /
                                                                              PEAK_F16_TFLOPS, 4),
-            "launches": launches, "flop": flop}
+            "launches": launches, "flop": flop, "forward_ab": fwd, "forward_flop": fflop}
 
 
 def bench_gru(torch, ge, datagen, dev, tm):

@@ -3,7 +3,7 @@
 // F-wide intermediate accumulated chunk by chunk on chip and never written to
 // HBM ("Full-Depth MLP Megakernel + Fused Attention Preprocessing", "What
 // Worked": one kernel whose hidden activations stay in registers and are
-// accumulated in 64-wide chunks; "What Didn't Work" / "The Key Insight": that
+// accumulated in narrow chunks; "What Didn't Work" / "The Key Insight": that
 // kernel lost 15-41 % to library GEMMs on its GPU, so here it is an A/B variant
 // of the GEMM chain, measured, not the default).
 //
@@ -19,18 +19,23 @@
 //   one exchange with lane l ^ 32, and n stays in registers for the whole
 //   kernel (32 fragments).
 // * For each chunk of 64 hidden units: the wave forms u^T for 32 of them
-//   (eh picks which) against its 32 rows: 32 MFMAs with W_up^T rows from LDS.
+//   (eh picks which) against its 32 rows: 32 MFMAs with W_up^T rows from LDS,
+//   alternating between two accumulators so two chains are in flight.
 //   The accumulator of lane l holds u for row l % 32 and four runs of four
 //   consecutive units, so a = LeakyReLU^2(u) goes to a small LDS tile [64 rows
 //   x 64 units] as 8-byte stores.  After a workgroup barrier every wave adds
 //   a W_down for its 32 rows and its 256 output columns: 8 output tiles x 4 k
 //   steps, the a fragment read once per k step, W_down^T rows from LDS.
-// * The next chunk's W_up^T and W_down^T slices are loaded into registers
-//   while the current chunk's MFMAs run, and written to LDS behind the
-//   barriers.  The kernel reads the weights as transposed copies that a small
-//   kernel writes first (unit-major W_up^T, output-major W_down^T), so every
-//   MFMA operand is a 16-byte LDS read of 8 consecutive k.
-// LDS: W_up^T chunk 64 KB, W_down^T chunk 64 KB, a tile 8 KB.
+// * The weight slices stream from global memory straight into LDS (buffer
+//   loads that write LDS, no register round trip): the next chunk's W_up^T
+//   while this chunk's down-projection MFMAs run, the next W_down^T while the
+//   next up-projection runs.  Each lane loads the 16 bytes that belong at its
+//   LDS position, so the swizzle is folded into the global offset.  The kernel reads the weights as transposed copies that a
+//   small kernel writes first (unit-major W_up^T, output-major W_down^T), so
+//   every MFMA operand is a 16-byte LDS read of 8 consecutive k.  Per CU the
+//   weights stream at 64 bytes of weights per 4 x 1,024 FLOP, which is what
+//   bounds the kernel: each 64-row block reads all of both matrices.
+// LDS: W_up^T slice 64 KB, W_down^T slice 64 KB, a tile 8 KB.
 #include "common.h"
 
 namespace ge {
@@ -41,14 +46,15 @@ typedef uint32_t mk_u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) mk_u32x4 lds_mk_u32x4;
 typedef uint32_t mk_u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) mk_u32x2 lds_mk_u32x2;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int MD = 512;       // model width the kernel is built for
 constexpr int MC = 64;        // hidden units per chunk
 constexpr int MBR = 64;       // rows per block
 constexpr int MKS = MD / 16;  // 16-wide k steps over D
-constexpr int WU_BYTES = MC * MD * 2;
-constexpr int WD_BYTES = MD * MC * 2;
-constexpr int AS_BYTES = MBR * MC * 2;
+constexpr int WU_BYTES = MC * MD * 2;   // the W_up^T slice [MC][MD]
+constexpr int WD_BYTES = MD * MC * 2;   // the W_down^T slice [MD][MC]
+constexpr int AS_BYTES = MBR * MC * 2;  // the a tile [MBR][MC]
 
 template <typename T> struct MkMfma;
 template <> struct MkMfma<bf16_t> {
@@ -64,17 +70,16 @@ template <> struct MkMfma<half_t> {
   }
 };
 
-// 16-byte chunk c of a 1 KB W_up^T row r sits at chunk c ^ (r & 15); of a 128-byte
-// row (W_down^T, a tile) at c ^ ((r / 2) & 7): the 16 lanes of one fragment
-// read hit 16 distinct bank groups
+// 16-byte chunk c of a 1 KB W_up^T row r sits at chunk c ^ (r & 15); of a
+// 128-byte row (W_down^T, the a tile) at c ^ ((r / 2) & 7): the 16 lanes of one
+// fragment read hit 16 distinct bank groups.  Both maps are their own inverse.
 __device__ __forceinline__ int swz_wu(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz_128(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 template <typename T>
-__device__ __forceinline__ T lrelu_sq(float u, float slope, float *a_f) {
+__device__ __forceinline__ T lrelu_sq(float u, float slope) {
   const float t = u > 0.f ? u : slope * u;
-  *a_f = t * t;
-  return from_f32<T>(*a_f);
+  return from_f32<T>(t * t);
 }
 
 }  // namespace
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(256, 1) void mlp_block_fused_kernel(const T *__rest
                                                                  T *__restrict__ u_out, T *__restrict__ a_out) {
   typedef typename MkMfma<T>::V V;
   __shared__ __attribute__((aligned(1024))) char smem[WU_BYTES + WD_BYTES + AS_BYTES];
-  char *Wu = smem, *Wd = smem + WU_BYTES, *As = smem + WU_BYTES + WD_BYTES;
+  char *const Wu = smem, *const Wd = smem + WU_BYTES, *const As = smem + WU_BYTES + WD_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rh = wave & 1, eh = wave >> 1;
   const int lr = lane & 31, lh = lane >> 5;
@@ -118,48 +123,41 @@ __global__ __launch_bounds__(256, 1) void mlp_block_fused_kernel(const T *__rest
   const bool rok = row < rows;
   const int nch = F / MC;
 
-  // ---- stage the first chunk's weights ------------------------------------
-  mk_u32x4 stg[16];
-  auto load_wu = [&](int c) {
+  // ---- weight slices: buffer loads that write LDS ---------------------------
+  // a wave's load instruction fills 1 KB of LDS, lane i the 16 bytes at i * 16;
+  // a slice is 64 such instructions, 16 per wave
+  const __amdgpu_buffer_rsrc_t rwu = __builtin_amdgcn_make_buffer_rsrc((void *)wut, (short)0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rwd = __builtin_amdgcn_make_buffer_rsrc((void *)wdt, (short)0, 0x7fffffff, 0x00020000);
+  auto issue_wu = [&](int c) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int i = tid + 256 * j, rr = i >> 6, cc = i & 63;
-      stg[j] = *(const mk_u32x4 *)(wut + (int64_t)(c * MC + rr) * MD + cc * 8);
+      const int ins = wave * 16 + j, p = ins * 64 + lane;  // LDS chunk position this lane fills
+      const int rr = p >> 6, cc = swz_wu(rr, p & 63);
+      const uint32_t vo = (uint32_t)(((int64_t)(c * MC + rr) * MD + cc * 8) * (int64_t)sizeof(T));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rwu, (lds_void_t *)(Wu + ins * 1024), 16, vo, 0, 0, 0);
     }
   };
-  auto store_wu = [&]() {
+  auto issue_wd = [&](int c) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int i = tid + 256 * j, rr = i >> 6, cc = i & 63;
-      *(lds_mk_u32x4 *)(Wu + rr * 1024 + swz_wu(rr, cc) * 16) = stg[j];
+      const int ins = wave * 16 + j, p = ins * 64 + lane;
+      const int e = p >> 3, cc = swz_128(e, p & 7);
+      const uint32_t vo = (uint32_t)(((int64_t)e * F + c * MC + cc * 8) * (int64_t)sizeof(T));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rwd, (lds_void_t *)(Wd + ins * 1024), 16, vo, 0, 0, 0);
     }
   };
-  auto load_wd = [&](int c) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int i = tid + 256 * j, e = i >> 3, cc = i & 7;
-      stg[j] = *(const mk_u32x4 *)(wdt + (int64_t)e * F + c * MC + cc * 8);
-    }
-  };
-  auto store_wd = [&]() {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int i = tid + 256 * j, e = i >> 3, cc = i & 7;
-      *(lds_mk_u32x4 *)(Wd + e * 128 + swz_128(e, cc) * 16) = stg[j];
-    }
-  };
-  load_wu(0);
-  store_wu();
-  load_wd(0);
+  issue_wu(0);
+  issue_wd(0);
 
   // ---- RMSNorm in the fragment layout --------------------------------------
   V nf[MKS];
   {
-    const T *xr = x + row * MD + 8 * lh;
+    // rows past the end read the last row and are never stored
+    const T *xr = x + (rok ? row : rows - 1) * MD + 8 * lh;
     float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < MKS; ++s) {
-      nf[s] = rok ? *(const V *)(xr + 16 * s) : V{};
+      nf[s] = *(const V *)(xr + 16 * s);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = to_f32(nf[s][e]);
@@ -180,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void mlp_block_fused_kernel(const T *__rest
       }
     }
   }
-  store_wd();
+  __builtin_amdgcn_s_waitcnt(0x0070);  // this wave's slices are in LDS
   __syncthreads();
 
   f32x16 yacc[8];
@@ -189,61 +187,59 @@ __global__ __launch_bounds__(256, 1) void mlp_block_fused_kernel(const T *__rest
 #pragma unroll
     for (int e = 0; e < 16; ++e) yacc[t][e] = 0.f;
 
+  const int ar = 32 * rh + lr;  // this lane's row of the a tile
   for (int c = 0; c < nch; ++c) {
     const bool more = c + 1 < nch;
-    if (more) load_wu(c + 1);
-    // u^T for units 32 eh .. +31 of the chunk against this wave's 32 rows
-    f32x16 uacc;
+    // u^T for units 32 eh .. +31 of the chunk against this wave's 32 rows, the
+    // k steps alternating between two accumulators (two independent chains)
+    f32x16 ua, ub;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) uacc[e] = 0.f;
+    for (int e = 0; e < 16; ++e) ua[e] = ub[e] = 0.f;
     {
       const int ur = 32 * eh + lr;
       const char *wrow = Wu + ur * 1024;
 #pragma unroll
-      for (int s = 0; s < MKS; ++s) {
-        const V p = __builtin_bit_cast(V, *(const lds_mk_u32x4 *)(wrow + swz_wu(ur, 2 * s + lh) * 16));
-        uacc = MkMfma<T>::mma(p, nf[s], uacc);
+      for (int s = 0; s < MKS; s += 2) {
+        const V p0 = __builtin_bit_cast(V, *(const lds_mk_u32x4 *)(wrow + swz_wu(ur, 2 * s + lh) * 16));
+        const V p1 = __builtin_bit_cast(V, *(const lds_mk_u32x4 *)(wrow + swz_wu(ur, 2 * s + 2 + lh) * 16));
+        ua = MkMfma<T>::mma(p0, nf[s], ua);
+        ub = MkMfma<T>::mma(p1, nf[s + 1], ub);
       }
     }
-    // lane: row 32 rh + lr, units 32 eh + 8 g + 4 lh + (0..3), g = 0..3
-    {
-      const int ar = 32 * rh + lr;
+    // lane: row ar, units 32 eh + 8 g + 4 lh + (0..3), g = 0..3
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        T av[4], uv[4];
+    for (int g = 0; g < 4; ++g) {
+      T av[4], uv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float af;
-          av[q] = lrelu_sq<T>(uacc[4 * g + q], slope, &af);
-          uv[q] = from_f32<T>(uacc[4 * g + q]);
-        }
-        const int unit = 32 * eh + 8 * g + 4 * lh;
-        *(lds_mk_u32x2 *)(As + ar * 128 + swz_128(ar, unit >> 3) * 16 + 8 * lh) = __builtin_bit_cast(mk_u32x2, av);
-        if (u_out && rok) *(mk_u32x2 *)(u_out + row * F + c * MC + unit) = __builtin_bit_cast(mk_u32x2, uv);
-        if (a_out && rok) *(mk_u32x2 *)(a_out + row * F + c * MC + unit) = __builtin_bit_cast(mk_u32x2, av);
+      for (int q = 0; q < 4; ++q) {
+        const float u = ua[4 * g + q] + ub[4 * g + q];
+        av[q] = lrelu_sq<T>(u, slope);
+        uv[q] = from_f32<T>(u);
       }
+      const int unit = 32 * eh + 8 * g + 4 * lh;
+      *(lds_mk_u32x2 *)(As + ar * 128 + swz_128(ar, unit >> 3) * 16 + 8 * lh) = __builtin_bit_cast(mk_u32x2, av);
+      if (u_out && rok) *(mk_u32x2 *)(u_out + row * F + c * MC + unit) = __builtin_bit_cast(mk_u32x2, uv);
+      if (a_out && rok) *(mk_u32x2 *)(a_out + row * F + c * MC + unit) = __builtin_bit_cast(mk_u32x2, av);
     }
+    // the a tile is complete, W_up^T is read, W_down^T of this chunk has landed
+    __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
-    if (more) {
-      store_wu();
-      load_wd(c + 1);
-    }
+    if (more) issue_wu(c + 1);
     // y^T += W_down^T a^T for output columns 256 eh .. +255 and this wave's rows
-    {
-      const int ar = 32 * rh + lr;
 #pragma unroll
-      for (int ks = 0; ks < MC / 16; ++ks) {
-        const V q = __builtin_bit_cast(V, *(const lds_mk_u32x4 *)(As + ar * 128 + swz_128(ar, 2 * ks + lh) * 16));
+    for (int ks = 0; ks < MC / 16; ++ks) {
+      const V q = __builtin_bit_cast(V, *(const lds_mk_u32x4 *)(As + ar * 128 + swz_128(ar, 2 * ks + lh) * 16));
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int er = 256 * eh + 32 * t + lr;
-          const V p = __builtin_bit_cast(V, *(const lds_mk_u32x4 *)(Wd + er * 128 + swz_128(er, 2 * ks + lh) * 16));
-          yacc[t] = MkMfma<T>::mma(p, q, yacc[t]);
-        }
+      for (int t = 0; t < 8; ++t) {
+        const int er = 256 * eh + 32 * t + lr;
+        const V p = __builtin_bit_cast(V, *(const lds_mk_u32x4 *)(Wd + er * 128 + swz_128(er, 2 * ks + lh) * 16));
+        yacc[t] = MkMfma<T>::mma(p, q, yacc[t]);
       }
     }
+    // W_down^T and the a tile are read, W_up^T of the next chunk has landed
+    __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
-    if (more) store_wd();
+    if (more) issue_wd(c + 1);
   }
 
   // ---- residual and store: lane holds y[row][256 eh + 32 t + 8 g + 4 lh + q] ----
@@ -285,8 +281,8 @@ int block_fused_launch(const ge_block_fused_args &a, hipStream_t s) {
     set_error("mlp_block_fwd_fused: D must be %d (got %lld)", MD, (long long)a.D);
     return GE_E_UNSUPPORTED;
   }
-  if (a.F < MC || a.F % MC != 0 || a.F > (1 << 20)) {
-    set_error("mlp_block_fwd_fused: F must be a positive multiple of %d", MC);
+  if (a.F < 64 || a.F % 64 != 0 || a.F > (1 << 20)) {
+    set_error("mlp_block_fwd_fused: F must be a positive multiple of 64");
     return GE_E_UNSUPPORTED;
   }
   if (a.rows / MBR >= 0x7fffffff) {
