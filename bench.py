@@ -249,7 +249,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(nn_tflops, 1), "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(nn_tflops / PEAK_F16_TFLOPS, 4),
                 "traffic": TRAFFIC_BY_SOURCE.get(sha),
-                "kernel": "gemm_w4_kernel<f16, NN, 256x128 tile> (fwd2 of the step, 4096x2048x2048)",
+                "kernel": "gemm_x8_kernel<f16, NN, 256x128 tile> (fwd2 of the step, 4096x2048x2048)",
                 "avg_launch_us": round(nn_us, 2), "launch_cv": round(nn_cv, 4),
                 "algorithmic_flop": f_nn, "gemm_source_sha": sha,
                 "measured_clock_ghz": clock,

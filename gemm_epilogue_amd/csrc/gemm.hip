@@ -238,15 +238,16 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart) {
     const bool a_mc = a.layout == GE_TN, b_mc = a.layout != GE_NT;
     gp.clamp = gp.a_vec && gp.b_vec && a.M >= v && a.N >= v && (!a_mc || a.M % v == 0) && (!b_mc || a.N % v == 0);
   }
-  // the eight-wave 256x256 kernel takes the plan's 256x256 tiles (same tiles
-  // and splits, so the same workspace) when every tile is whole, K is whole
-  // 64-wide k-tiles, the rows are 16-byte aligned and the buffer offsets of
-  // one tile stay below 2^31 bytes
-  if ((a.ab_type == GE_F16 || a.ab_type == GE_BF16) && pl.bm == 256 && pl.bn == 256 && a.M % 256 == 0 &&
-      a.N % 256 == 0 && a.K % 64 == 0 && gp.a_vec && gp.b_vec) {
-    auto span = [&](bool kc, int64_t ld) { return kc ? (255 * ld + a.K) * es : (a.K * ld + 256) * es; };
+  // the eight-wave kernel takes the plan's 256x256 or 256x128 tiles (same
+  // tiles and splits, so the same workspace) when every tile is whole, K is
+  // whole 64-wide k-tiles, the rows are 16-byte aligned and the buffer offsets
+  // of one tile stay below 2^31 bytes
+  if ((a.ab_type == GE_F16 || a.ab_type == GE_BF16) && pl.bm == 256 && (pl.bn == 256 || pl.bn == 128) &&
+      a.M % 256 == 0 && a.N % pl.bn == 0 && a.K % 64 == 0 && gp.a_vec && gp.b_vec) {
+    auto span = [&](bool kc, int64_t ld, int64_t w) { return kc ? ((w - 1) * ld + a.K) * es : (a.K * ld + w) * es; };
     const bool a_kc = a.layout != GE_TN, b_kc = a.layout == GE_NT;
-    if (span(a_kc, a.lda) < ((int64_t)1 << 31) && span(b_kc, a.ldb) < ((int64_t)1 << 31)) pl.x8 = 1;
+    if (span(a_kc, a.lda, 256) < ((int64_t)1 << 31) && span(b_kc, a.ldb, pl.bn) < ((int64_t)1 << 31))
+      pl.x8 = pl.bn == 256 ? 1 : 2;
   }
   gp.tiles_m = pl.tiles_m;
   gp.tiles_n = pl.tiles_n;

@@ -1176,19 +1176,25 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int X8_BK = 64;                     // k per stage
-constexpr int X8_TILE = 256 * X8_BK * 2;      // bytes of one operand tile of one stage
-constexpr int X8_STAGE = 2 * X8_TILE;
-constexpr int X8_SMEM = 2 * X8_STAGE > 128 * (256 + 4) * 4 ? 2 * X8_STAGE : 128 * (256 + 4) * 4;
+constexpr int X8_BK = 64;  // k per stage
+
+// LDS bytes of one stage (A tile 256 x 64, B tile BN x 64) and of the kernel
+// (two stages, or the FP32 staging of half the tile for the epilogue)
+template <int BN> constexpr int x8_stage() { return (256 + BN) * X8_BK * 2; }
+template <int BN> constexpr int x8_smem() {
+  return 2 * x8_stage<BN>() > 128 * (BN + 4) * 4 ? 2 * x8_stage<BN>() : 128 * (BN + 4) * 4;
+}
 
 __device__ __forceinline__ int x8_kc_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int x8_mc_swz(int k) { return 2 * (k & 3); }
 
-// Per-lane byte offsets of the two instruction parities of one operand tile
-// (instruction ins covers rows 8 ins .. +7 of a k-contiguous tile, k-rows
-// 2 ins, 2 ins + 1 of an m/n-contiguous one); the rest of the address is
-// uniform and goes in the scalar offset.
-template <bool KC>
+// Per-lane byte offsets of the two instruction parities of one operand tile.
+// A k-contiguous tile: instruction ins covers rows 8 ins .. +7.  An
+// m/n-contiguous tile W wide: its k-rows are 2 W bytes, so instruction ins
+// covers k-rows (1024 / 2W) ins .. + 1024 / 2W - 1 (two k-rows at W = 256,
+// four at W = 128).  The rest of the address is uniform and goes in the
+// scalar offset.
+template <bool KC, int W>
 __device__ __forceinline__ void x8_lane_offsets(int64_t ld, int es, int lane, uint32_t (&vo)[2]) {
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -1196,51 +1202,66 @@ __device__ __forceinline__ void x8_lane_offsets(int64_t ld, int es, int lane, ui
       const int row = par * 8 + (lane >> 3);
       const int c = (lane & 7) ^ x8_kc_swz(row);
       vo[par] = (uint32_t)(((lane >> 3) * ld + 8 * c) * es);
-    } else {
+    } else if constexpr (W == 256) {
       const int k = par * 2 + (lane >> 5);
       const int sl = ((lane & 31) >> 1) ^ x8_mc_swz(k);
       vo[par] = (uint32_t)(((lane >> 5) * ld + 16 * sl + 8 * (lane & 1)) * es);
+    } else {
+      // four k-rows per instruction: k & 3 = lane >> 4 for every instruction
+      const int kl = lane >> 4;
+      const int sl = ((lane & 15) >> 1) ^ x8_mc_swz(kl);
+      vo[par] = (uint32_t)((kl * ld + 16 * sl + 8 * (lane & 1)) * es);
     }
   }
 }
 
 // base points at the tile's first row (k-contiguous) or first column (m/n-contiguous)
-template <bool KC>
+template <bool KC, int W>
 __device__ __forceinline__ void x8_load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int es, int k0, char *lds_tile, int ins,
                                         const uint32_t (&vo)[2]) {
-  const uint32_t so = KC ? (uint32_t)(((int64_t)(ins * 8) * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * 2) * ld * es);
+  constexpr int KPI = 1024 / (2 * W);  // k-rows per instruction of an m/n-contiguous tile
+  const uint32_t so = KC ? (uint32_t)(((int64_t)(ins * 8) * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * KPI) * ld * es);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + ins * 1024), 16, vo[ins & 1], so, 0, 0);
 }
 
 // fragment of the 32x32x16 MFMA: rows r .. r+31 of the operand, k block kb
 // (16 k) of the stage; lane l gets row r + l % 32, k = 16 kb + 8 (l / 32) .. +7
-template <typename V, bool KC>
+template <typename V, bool KC, int W>
 __device__ __forceinline__ V x8_frag(const char *tile, int r, int kb, int lane) {
   if constexpr (KC) {
     const int row = r + (lane & 31);
     const int c = (2 * kb + (lane >> 5)) ^ x8_kc_swz(row);
     return __builtin_bit_cast(V, *(const lds_u32x4 *)(tile + row * 128 + c * 16));
   } else {
+    constexpr int ROWB = 2 * W;  // bytes of one k-row
     const int G = lane >> 4, j = lane & 15;
     const int k = 16 * kb + 8 * (G >> 1) + (j >> 2);
     const int slot = (r >> 4) + (G & 1);
-    const char *p0 = tile + k * 512 + ((slot ^ x8_mc_swz(k)) * 32) + 8 * (j & 3);
-    const char *p1 = tile + (k + 4) * 512 + ((slot ^ x8_mc_swz(k + 4)) * 32) + 8 * (j & 3);
+    const char *p0 = tile + k * ROWB + ((slot ^ x8_mc_swz(k)) * 32) + 8 * (j & 3);
+    const char *p1 = tile + (k + 4) * ROWB + ((slot ^ x8_mc_swz(k + 4)) * 32) + 8 * (j & 3);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
     return __builtin_bit_cast(V, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 }
 
-template <typename T, int LAYOUT>
+// BN = 256: wave tile 128 x 64 (waves 2 x 4); BN = 128: 64 x 64 (waves 4 x 2),
+// which fills the 256 CUs at 4096 x 2048 and carries the dgrad's column sums
+template <typename T, int LAYOUT, int BN>
 __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256, NT = 512;
+  constexpr int BM = 256, NT = 512;
+  constexpr int WTM = BN == 256 ? 128 : 64;
+  constexpr int FA = WTM / 32;  // A fragments (32-row blocks) per wave
   constexpr bool A_KC = (LAYOUT != GE_TN);
   constexpr bool B_KC = (LAYOUT == GE_NT);
+  constexpr int TILE_A = BM * X8_BK * 2;
+  constexpr int STAGE = x8_stage<BN>();
+  constexpr int BPW = BN / 64;  // B tile load instructions per wave
   typedef typename Mfma32<T>::V V;
-  __shared__ __attribute__((aligned(1024))) char smem[X8_SMEM];
+  __shared__ __attribute__((aligned(1024))) char smem[x8_smem<BN>()];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
+  const int wm0 = BN == 256 ? (wave >> 2) * 128 : (wave >> 1) * 64;
+  const int wn0 = BN == 256 ? (wave & 3) * 64 : (wave & 1) * 64;
   int bm0, bn0, split;
   block_work(p, BM, BN, bm0, bn0, split);
   const int nk = p.K / X8_BK;
@@ -1253,50 +1274,49 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)Ab, (short)0, 0x7fffffff, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bb, (short)0, 0x7fffffff, 0x00020000);
   uint32_t voa[2], vob[2];
-  x8_lane_offsets<A_KC>(p.lda, es, lane, voa);
-  x8_lane_offsets<B_KC>(p.ldb, es, lane, vob);
-  // a stage: 32 instructions per operand tile, 4 + 4 per wave
+  x8_lane_offsets<A_KC, BM>(p.lda, es, lane, voa);
+  x8_lane_offsets<B_KC, BN>(p.ldb, es, lane, vob);
+  // a stage: 32 instructions for the A tile (4 per wave), BN / 8 for the B tile
   auto issue = [&](int t) {
-    char *st = smem + (t & 1) * X8_STAGE;
+    char *st = smem + (t & 1) * STAGE;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ins = wave * 4 + u;
-      x8_load<A_KC>(ra, p.lda, es, t * X8_BK, st, ins, voa);
-      x8_load<B_KC>(rb, p.ldb, es, t * X8_BK, st + X8_TILE, ins, vob);
-    }
+    for (int u = 0; u < 4; ++u) x8_load<A_KC, BM>(ra, p.lda, es, t * X8_BK, st, wave * 4 + u, voa);
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) x8_load<B_KC, BN>(rb, p.ldb, es, t * X8_BK, st + TILE_A, wave * BPW + u, vob);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[FA][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FA; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  V fa0[4], fb0[2], fa1[4], fb1[2];
-  auto rd = [&](const char *st, int kb, V(&fa)[4], V(&fb)[2]) {
+  V fa0[FA], fb0[2], fa1[FA], fb1[2];
+  auto rd = [&](const char *st, int kb, V(&fa)[FA], V(&fb)[2]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = x8_frag<V, B_KC>(st + X8_TILE, wn0 + 32 * j, kb, lane);
+    for (int j = 0; j < 2; ++j) fb[j] = x8_frag<V, B_KC, BN>(st + TILE_A, wn0 + 32 * j, kb, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = x8_frag<V, A_KC>(st, wm0 + 32 * i, kb, lane);
+    for (int i = 0; i < FA; ++i) fa[i] = x8_frag<V, A_KC, BM>(st, wm0 + 32 * i, kb, lane);
   };
   // the B fragment goes first, so lane l owns C[m = l % 32][n = 8 (e / 4) + 4 (l / 32) + e % 4]
-  auto mma = [&](const V(&fa)[4], const V(&fb)[2]) {
+  auto mma = [&](const V(&fa)[FA], const V(&fb)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FA; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = Mfma32<T>::mma(fb[j], fa[i], acc[i][j]);
   };
-  constexpr int NR = (A_KC ? 4 : 8) + (B_KC ? 2 : 4);  // LDS read instructions per k block
-  auto phase = [&](const char *st, int kb, V(&fan)[4], V(&fbn)[2], const V(&fac)[4], const V(&fbc)[2],
+  constexpr int NM = 2 * FA;                                // MFMAs per k block
+  constexpr int NR = (A_KC ? FA : 2 * FA) + (B_KC ? 2 : 4);  // LDS read instructions per k block
+  auto phase = [&](const char *st, int kb, V(&fan)[FA], V(&fbn)[2], const V(&fac)[FA], const V(&fbc)[2],
                    bool do_mma) {
     rd(st, kb, fan, fbn);
     if (do_mma) {
       mma(fac, fbc);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x100, (NR + 7) / 8, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+      for (int u = 0; u < NM; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, (NR + NM - 1) / NM, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1308,7 +1328,7 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
     __syncthreads();
     if (t + 1 < kt1) issue(t + 1);
     __builtin_amdgcn_sched_barrier(0);
-    const char *st = smem + (t & 1) * X8_STAGE;
+    const char *st = smem + (t & 1) * STAGE;
     phase(st, 0, fa0, fb0, fa1, fb1, t > kt0);  // with the MFMAs of the previous stage's last block
     phase(st, 1, fa1, fb1, fa0, fb0, true);
     phase(st, 2, fa0, fb0, fa1, fb1, true);
@@ -1317,15 +1337,16 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
   if (kt0 < kt1) mma(fa1, fb1);
   __builtin_amdgcn_s_waitcnt(0x0070);
   __syncthreads();
-  store_tile_staged<BM, BN, NT, 2, 0, false>(p, smem, tid, bm0, bn0, split, [&](int pass, float *cs) {
+  // the staged epilogue in two passes of 128 rows: waves 0-3 hold rows 0..127
+  store_tile_staged<BM, BN, NT, 2, 0, (BN < 256)>(p, smem, tid, bm0, bn0, split, [&](int pass, float *cs) {
     if ((wave >> 2) == pass) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FA; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int r = 32 * i + (lane & 31);
+            const int r = (wm0 - 128 * pass) + 32 * i + (lane & 31);
             const int c = wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
             const f32x16 &v = acc[i][j];
             *(f32x4 *)(cs + r * (BN + 4) + c) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
@@ -1336,7 +1357,7 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
 
 // ---- launch plan and per-type launchers ---------------------------------------
 struct Plan {
-  int x8;      // the eight-wave 256x256 kernel (k-tiles of 64)
+  int x8;      // the eight-wave kernel (k-tiles of 64): 1 for 256x256 tiles, 2 for 256x128
   int bm, bn;  // tile: 256x256, 256x128, 128x128, 64x64, or 128x16 for N <= 16
   int BK;
   int tiles_m, tiles_n, nk, splits, kps;
@@ -1351,8 +1372,12 @@ void launch_t(const Plan &pl, const GemmParams &gp, hipStream_t s) {
   // ping-pong kernel when both are k-contiguous (NT) and for short k ranges
   // (split-K blocks of fewer than 16 k-tiles)
   if constexpr (sizeof(T) == 2) {
-    if (pl.x8) {
-      hipLaunchKernelGGL((gemm_x8_kernel<T, LAYOUT>), grid, dim3(512), 0, s, gp);
+    if (pl.x8 == 1) {
+      hipLaunchKernelGGL((gemm_x8_kernel<T, LAYOUT, 256>), grid, dim3(512), 0, s, gp);
+      return;
+    }
+    if (pl.x8 == 2) {
+      hipLaunchKernelGGL((gemm_x8_kernel<T, LAYOUT, 128>), grid, dim3(512), 0, s, gp);
       return;
     }
   }

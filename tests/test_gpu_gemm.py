@@ -206,7 +206,9 @@ def test_cfg1_4096_sampled(ge, layout):
 # ----------- shapes that take the eight-wave 256x256 kernel (32x32x16 MFMA) --
 # whole 256x256 tiles and K a multiple of 64: unsplit when the tiles fill the
 # GPU, split-K (then the finishing pass applies the epilogue) when they do not
-X8 = [(4096, 3072, 256), (3072, 4096, 512), (512, 512, 16384)]
+# 256x256 tiles for the first three; 256x128 tiles (eight waves, 64x64 each)
+# for the last two, the shapes of the 784-2048-2048-10 step's middle layer
+X8 = [(4096, 3072, 256), (3072, 4096, 512), (512, 512, 16384), (4096, 2048, 2048), (4096, 1536, 1536)]
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
