@@ -231,7 +231,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- roofline: the dominant kernel of the step -------------------------
-    # the 256x128 four-wave GEMM-epilogue kernel runs the step's two
+    # the eight-wave 256x128 GEMM-epilogue kernel runs the step's two
     # 4096x2048x2048 GEMMs (forward H2 = relu(H1 W2 + b2) and the masked
     # dgrad); its forward launch is replayed with the step's own operands
     views = tr.workspace_views(BATCH)
