@@ -36,6 +36,7 @@ int gru_bwd_launch(const float *dh_out, const float *carry, const float *R, cons
                    const float *GH, const float *hp, int B, int H, half_t *dGH, half_t *dGI, float *dh_dir,
                    hipStream_t s);
 bool gru_persist_supported(int64_t B, int64_t H);
+int64_t gru_sync_bytes();
 int gru_rec_fwd_launch(const float *GI, const half_t *Wh, const float *bh, int B, int H, int T, float *GH, float *R,
                        float *Z, float *N, float *HS, half_t *H16, unsigned *sync, hipStream_t s);
 int gru_rec_bwd_launch(const float *dh_out, const half_t *Wh, const float *R, const float *Z, const float *N,
@@ -128,8 +129,8 @@ GruLayout layout_of(const ge_gru_desc *d) {
   L.emb_off = o;
   L.emb_ws = embedding_grad_ws_bytes(NT, V);
   o = align_up(o + L.emb_ws);
-  L.sync_off = o;  // barrier counter and error word of the persistent recurrence
-  o = align_up(o + 8);
+  L.sync_off = o;  // barrier counters and error word of the persistent recurrence
+  o = align_up(o + gru_sync_bytes());
   L.total = o;
   return L;
 }

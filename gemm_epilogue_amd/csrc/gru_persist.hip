@@ -5,29 +5,32 @@
 // section "Keep state resident"; the tiny serialized per-timestep jobs are
 // the cost that section and "Why This Belongs in a Game Engine" point at).
 //
-// Block b of the NB = H / 16 blocks owns hidden units u0 = 16 b .. u0 + 15.
-//   forward step t:  GH[:, g H + u0 + j] = h16_{t-1} W_h[:, g H + u0 + j] + b_h
-//                    for the three gate blocks g (r, z, n) and j < 16 -- a
-//                    [B x H] x [H x 48] product on MFMA with the 48 columns of
-//                    W_h in LDS -- then the gate arithmetic for its units, the
-//                    stores of r, z, n, h, the FP16 copy of h and GH; then one
-//                    grid-wide barrier (every block needs all of h16_t next).
-//                    A lane's h_{t-1} is its own previous output, kept in
-//                    registers, and the next step's GI is fetched before the
-//                    barrier; all of a lane's h16 loads are issued before the
-//                    first MFMA, so a step waits on memory once.
-//   backward step t: dh = dh_out + carry for its units (the carry is the
-//                    block's own, kept in registers), the gate backward, the
-//                    stores of dGH, dGI; one grid-wide barrier (every block
-//                    needs all of dGH_t); then carry = dh z + dGH_t W_h[u0 +
-//                    j, :]^T, a [B x 3H] x [3H x 16] product with the 16 rows
-//                    of W_h in LDS, its 3H columns split over four wave groups
-//                    whose partial sums meet in LDS in a fixed order.
-// Wave group w % 4 of a block handles batch rows 16 (w % 4) .. + 15, so B <= 64
-// and B % 16 == 0; H = 256 KB for KB = 1 .. 4, so the W_h slice (48 H or
-// 16 x 3H halves) fits LDS and a lane's loads of one step fit its registers.
-// The gate arithmetic and every stored tensor are those of gru_fwd_kernel /
-// gru_bwd_kernel (seq.hip); only the GEMM's summation order differs.
+// Block (g, q) of the (H / 16) x (B / 16) blocks owns hidden units
+// u0 = 16 g .. u0 + 15 for batch rows 16 q .. 16 q + 15; a row group q is an
+// independent recurrence, so its H / 16 blocks meet at a barrier of their own.
+//   forward step t:  GH[rows, g' H + u0 + j] = h16_{t-1}[rows] W_h[:, g' H + u0 + j]
+//                    + b_h for the three gate blocks g' (r, z, n) and j < 16 --
+//                    a [16 x H] x [H x 48] product on MFMA with the 48 columns
+//                    of W_h in LDS, its H split over the block's four waves and
+//                    the partial sums added in LDS in wave order -- then the
+//                    gate arithmetic, the stores of r, z, n, h, the FP16 copy
+//                    of h and GH, and the row group's barrier (each of its
+//                    blocks needs all of h16_t for those rows next).  The
+//                    lane's h_{t-1} is its own previous output (registers),
+//                    the next step's GI is fetched before the barrier, and a
+//                    wave issues all of its h16 loads before its first MFMA.
+//   backward step t: dh = dh_out + carry for the block's units and rows (the
+//                    carry stays in registers), the gate backward, the stores
+//                    of dGH, dGI, the row group's barrier, then carry = dh z +
+//                    dGH_t[rows] W_h[u0 + j, :]^T, a [16 x 3H] x [3H x 16]
+//                    product with the 16 rows of W_h in LDS, 3H split over
+//                    the four waves and summed in LDS in wave order.
+// Splitting the batch over blocks keeps each CU's per-step h16 (or dGH)
+// traffic to its own 16 rows.  B <= 64 and B % 16 == 0; H = 256 KB for
+// KB = 1 .. 4, so the W_h slice fits LDS and a lane's loads of one step fit
+// its registers.  The gate arithmetic and every stored tensor are those of
+// gru_fwd_kernel / gru_bwd_kernel (seq.hip); only the GEMM's summation order
+// differs.
 #include "common.h"
 #include "persist.h"
 
@@ -45,6 +48,10 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 15); }
 
 }  // namespace
 
+// barrier words: a counter per row group, 256 bytes apart, then the error word
+constexpr int kSyncStride = 64;  // unsigned words
+constexpr int kSyncWords = 5 * kSyncStride;
+
 template <int KB>
 __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__restrict__ GI, const half_t *__restrict__ Wh,
                                                              const float *__restrict__ bh, int B, int T,
@@ -52,11 +59,15 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
                                                              float *__restrict__ Z, float *__restrict__ Nn,
                                                              float *__restrict__ HS, half_t *__restrict__ H16,
                                                              unsigned *__restrict__ sync) {
-  constexpr int H = 256 * KB, H3 = 3 * H;
+  constexpr int H = 256 * KB, H3 = 3 * H, NS = 2 * KB;  // 32-wide k chunks per wave
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  half_t *w = (half_t *)smem;  // [48][H]: row c = gate c / 16, unit c % 16; k contiguous, chunks swizzled
+  half_t *w = (half_t *)smem;                   // [48][H]: row c = gate c / 16, unit c % 16; chunks swizzled
+  f32x4 *red = (f32x4 *)(smem + 48 * H * 2);    // [3 waves][3 gates][64]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int u0 = blockIdx.x * 16;
+  const int nug = H / 16;
+  const int ug = blockIdx.x % nug, rg = blockIdx.x / nug;
+  const int u0 = ug * 16;
+  unsigned *count = sync + kSyncStride * rg, *err = sync + 4 * kSyncStride;
   // W_h columns of this block, transposed into LDS: thread takes (k, gate),
   // reads the 16 units of row k of that gate block and writes them to 16 rows
   for (int p = tid; p < H * 3; p += 256) {
@@ -69,43 +80,51 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
       w[row * H + swz(row, k >> 3) * 8 + (k & 7)] = u < 8 ? a[u] : b[u - 8];
     }
   }
-  const int m = wave * 16 + (lane & 15);  // batch row of this lane
-  const int j0 = 4 * (lane >> 4);         // its four units within the block
-  const bool live = wave * 16 < B;
+  const int m = rg * 16 + (lane & 15);  // batch row of this lane
+  const int j0 = 4 * (lane >> 4);       // its four units within the block
+  const int k0 = wave * (H / 4);        // this wave's quarter of the contraction
   f32x4 bias[3], gi[3];
-  f32x4 hp = {0.f, 0.f, 0.f, 0.f};  // h_{t-1} of the lane's (row, units)
+  f32x4 hp = {0.f, 0.f, 0.f, 0.f};  // h_{t-1} of the lane's (row, units), wave 0
 #pragma unroll
   for (int g = 0; g < 3; ++g) bias[g] = *(const f32x4 *)(bh + g * H + u0 + j0);
-  if (live) {
+  if (wave == 0) {
 #pragma unroll
     for (int g = 0; g < 3; ++g) gi[g] = *(const f32x4 *)(GI + (int64_t)m * H3 + g * H + u0 + j0);
   }
   __syncthreads();
   for (int t = 0; t < T; ++t) {
-    if (live) {
-      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      if (t > 0) {
-        // h16_{t-1} row m: the lane's 8 k values of each 32-wide chunk
-        const half_t *hrow = H16 + ((int64_t)t * B + m) * H + 8 * (lane >> 4);
-        f16x8 hv[8 * KB];
+    f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (t > 0) {
+      // h16_{t-1} row m over this wave's quarter: the lane's 8 k of each 32-wide chunk
+      const half_t *hrow = H16 + ((int64_t)t * B + m) * H + k0 + 8 * (lane >> 4);
+      f16x8 hv[NS];
 #pragma unroll
-        for (int s = 0; s < 8 * KB; ++s) hv[s] = *(const f16x8 *)(hrow + 32 * s);
+      for (int s = 0; s < NS; ++s) hv[s] = *(const f16x8 *)(hrow + 32 * s);
 #pragma unroll
-        for (int s = 0; s < 8 * KB; ++s) {
-          const int c = 4 * s + (lane >> 4);
+      for (int s = 0; s < NS; ++s) {
+        const int c = (k0 + 32 * s) / 8 + (lane >> 4);
 #pragma unroll
-          for (int g = 0; g < 3; ++g) {
-            const int row = g * 16 + (lane & 15);
-            const f16x8 wv = *(const lds_f16x8_t *)(w + row * H + swz(row, c) * 8);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, hv[s], acc[g], 0, 0, 0);
-          }
+        for (int g = 0; g < 3; ++g) {
+          const int row = g * 16 + (lane & 15);
+          const f16x8 wv = *(const lds_f16x8_t *)(w + row * H + swz(row, c) * 8);
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, hv[s], acc[g], 0, 0, 0);
         }
       }
+      if (wave > 0) {
+#pragma unroll
+        for (int g = 0; g < 3; ++g) red[((wave - 1) * 3 + g) * 64 + lane] = acc[g];
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
       // lane holds GH[m][g H + u0 + j0 .. +3] (before the bias)
       const int64_t row = (int64_t)t * B + m;
       f32x4 gh[3], r, z, nn, hv;
 #pragma unroll
-      for (int g = 0; g < 3; ++g) gh[g] = acc[g] + bias[g];
+      for (int g = 0; g < 3; ++g) {
+        if (t > 0) acc[g] = ((acc[g] + red[g * 64 + lane]) + red[(3 + g) * 64 + lane]) + red[(6 + g) * 64 + lane];
+        gh[g] = acc[g] + bias[g];
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         r[q] = sigm(gi[0][q] + gh[0][q]);
@@ -127,33 +146,34 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
         for (int g = 0; g < 3; ++g) gi[g] = *(const f32x4 *)(GI + (row + B) * H3 + g * H + u0 + j0);
       }
     }
-    if (t + 1 < T && !grid_barrier(sync, (unsigned)((t + 1) * gridDim.x), sync + 1)) return;
+    if (t + 1 < T && !grid_barrier(count, (unsigned)((t + 1) * nug), err)) return;
   }
 }
 
 template <int KB>
-__global__ __launch_bounds__(1024, 1) void gru_rec_bwd_kernel(const float *__restrict__ dh_out,
-                                                              const half_t *__restrict__ Wh, const float *__restrict__ R,
-                                                              const float *__restrict__ Z, const float *__restrict__ Nn,
-                                                              const float *__restrict__ GH, const float *__restrict__ HS,
-                                                              int B, int T, half_t *__restrict__ dGH,
-                                                              half_t *__restrict__ dGI, unsigned *__restrict__ sync) {
+__global__ __launch_bounds__(256, 1) void gru_rec_bwd_kernel(const float *__restrict__ dh_out,
+                                                             const half_t *__restrict__ Wh, const float *__restrict__ R,
+                                                             const float *__restrict__ Z, const float *__restrict__ Nn,
+                                                             const float *__restrict__ GH, const float *__restrict__ HS,
+                                                             int B, int T, half_t *__restrict__ dGH,
+                                                             half_t *__restrict__ dGI, unsigned *__restrict__ sync) {
   constexpr int H = 256 * KB, H3 = 3 * H, KC = H3 / 8;  // 16-byte chunks per W row
-  constexpr int NS = KC / 16;                           // chunk groups (of 4) per wave group
+  constexpr int NS = KC / 16;                           // chunk groups (of 4) per wave
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  half_t *w = (half_t *)smem;                      // [16][3H]: rows u0 .. u0 + 15 of W_h, chunks swizzled
-  f32x4 *red = (f32x4 *)(smem + 16 * H3 * 2);      // [3][4][64] partial carries of wave groups 1..3
+  half_t *w = (half_t *)smem;                  // [16][3H]: rows u0 .. u0 + 15 of W_h, chunks swizzled
+  f32x4 *red = (f32x4 *)(smem + 16 * H3 * 2);  // [3 waves][64] partial carries
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = wave & 3, part = wave >> 2;
-  const int u0 = blockIdx.x * 16;
-  for (int p = tid; p < 16 * KC; p += 1024) {
+  const int nug = H / 16;
+  const int ug = blockIdx.x % nug, rg = blockIdx.x / nug;
+  const int u0 = ug * 16;
+  unsigned *count = sync + kSyncStride * rg, *err = sync + 4 * kSyncStride;
+  for (int p = tid; p < 16 * KC; p += 256) {
     const int u = p / KC, c = p % KC;
     *(f16x8 *)(w + u * H3 + swz(u, c) * 8) = *(const f16x8 *)(Wh + (int64_t)(u0 + u) * H3 + 8 * c);
   }
   const int m = rg * 16 + (lane & 15);
   const int j0 = 4 * (lane >> 4);
-  const bool live = rg * 16 < B;
-  const bool gate = live && part == 0;  // the waves that run the gate backward and own the carry
+  const bool gate = wave == 0;  // the wave that runs the gate backward and owns the carry
   f32x4 carry = {0.f, 0.f, 0.f, 0.f};
   f32x4 dho, r, z, nn, ghn, h0;
   auto fetch = [&](int t) {
@@ -198,40 +218,31 @@ __global__ __launch_bounds__(1024, 1) void gru_rec_bwd_kernel(const float *__res
     }
     if (t == 0) break;
     ++nbar;
-    if (!grid_barrier(sync, (unsigned)(nbar * gridDim.x), sync + 1)) return;
+    if (!grid_barrier(count, (unsigned)(nbar * nug), err)) return;
     // carry for step t-1: dh z + dGH_t[m, :] W_h[u0 + j, :]^T over the 3H
-    // columns; wave group `part` takes chunks part KC/4 .. (part + 1) KC/4
+    // columns; wave `wave` takes chunks wave KC/4 .. (wave + 1) KC/4
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
-      const half_t *grow = dGH + ((int64_t)t * B + m) * H3 + part * (H3 / 4) + 8 * (lane >> 4);
+    {
+      const half_t *grow = dGH + ((int64_t)t * B + m) * H3 + wave * (H3 / 4) + 8 * (lane >> 4);
       f16x8 gv[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) gv[s] = *(const f16x8 *)(grow + 32 * s);
       const int wr = lane & 15;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int c = part * (KC / 4) + 4 * s + (lane >> 4);
+        const int c = wave * (KC / 4) + 4 * s + (lane >> 4);
         const f16x8 wv = *(const lds_f16x8_t *)(w + wr * H3 + swz(wr, c) * 8);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, gv[s], acc, 0, 0, 0);
       }
-      if (part > 0) red[((part - 1) * 4 + rg) * 64 + lane] = acc;
+      if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
     }
     __syncthreads();
-    if (gate) carry = ((acc + red[rg * 64 + lane]) + red[(4 + rg) * 64 + lane]) + red[(8 + rg) * 64 + lane] + dd;
-    // the next writes to red follow the next grid barrier's workgroup barrier
+    if (gate) carry = ((acc + red[lane]) + red[64 + lane]) + red[128 + lane] + dd;
+    // the next writes to red follow the next barrier's workgroup barrier
   }
 }
 
 // ---- launchers ------------------------------------------------------------------
-bool gru_persist_supported(int64_t B, int64_t H) {
-  if (B < 1 || B > 64 || B % 16 != 0 || H % 256 != 0 || H < 256 || H > 1024) return false;
-  int dev = 0, coop = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  return H / 16 <= cus;
-}
-
 namespace {
 
 const void *fwd_kernel(int KB) {
@@ -252,19 +263,27 @@ const void *bwd_kernel(int KB) {
   }
 }
 
-int coop_launch(const void *fn, int slot, int blocks, int threads, size_t lds, void **args, hipStream_t s,
-                const char *what) {
-  // the dynamic LDS above the default limit has to be granted per kernel
+size_t fwd_lds(int H) { return (size_t)48 * H * 2 + (size_t)9 * 64 * 16; }
+size_t bwd_lds(int H) { return (size_t)16 * 3 * H * 2 + (size_t)3 * 64 * 16; }
+
+// the dynamic LDS above the default limit has to be granted per kernel
+bool grant(const void *fn, int slot, size_t lds) {
   static size_t granted[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (lds > granted[slot]) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-      (void)hipGetLastError();
-      set_error("%s: cannot grant %zu bytes of LDS", what, lds);
-      return GE_E_LAUNCH;
-    }
-    granted[slot] = lds;
+  if (lds <= granted[slot]) return true;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
   }
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(threads), args, (unsigned)lds, s);
+  granted[slot] = lds;
+  return true;
+}
+
+int coop_launch(const void *fn, int slot, int blocks, size_t lds, void **args, hipStream_t s, const char *what) {
+  if (!grant(fn, slot, lds)) {
+    set_error("%s: cannot grant %zu bytes of LDS", what, lds);
+    return GE_E_LAUNCH;
+  }
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(256), args, (unsigned)lds, s);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     set_error("%s: cooperative launch failed: %s", what, hipGetErrorString(e));
@@ -275,27 +294,52 @@ int coop_launch(const void *fn, int slot, int blocks, int threads, size_t lds, v
 
 }  // namespace
 
+int64_t gru_sync_bytes() { return (int64_t)kSyncWords * 4; }
+
+bool gru_persist_supported(int64_t B, int64_t H) {
+  if (B < 1 || B > 64 || B % 16 != 0 || H % 256 != 0 || H < 256 || H > 1024) return false;
+  int dev = 0, coop = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  // every block of either kernel must be resident at once
+  const int KB = (int)(H / 256), blocks = (int)(H / 16 * (B / 16));
+  const void *fns[2] = {fwd_kernel(KB), bwd_kernel(KB)};
+  const size_t lds[2] = {fwd_lds((int)H), bwd_lds((int)H)};
+  for (int i = 0; i < 2; ++i) {
+    int per_cu = 0;
+    if (!grant(fns[i], i * 4 + KB - 1, lds[i]) ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fns[i], 256, lds[i]) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    if ((int64_t)per_cu * cus < blocks) return false;
+  }
+  return true;
+}
+
 int fill_zero_launch(void *p, int64_t bytes, hipStream_t s);
 
-// sync: device unsigned [2] (barrier counter, error word), cleared here first
+// sync: device unsigned [gru_sync_bytes() / 4] (a barrier counter per row
+// group and the error word), cleared here first
 int gru_rec_fwd_launch(const float *GI, const half_t *Wh, const float *bh, int B, int H, int T, float *GH, float *R,
                        float *Z, float *N, float *HS, half_t *H16, unsigned *sync, hipStream_t s) {
-  int st = fill_zero_launch(sync, 2 * sizeof(unsigned), s);
+  int st = fill_zero_launch(sync, gru_sync_bytes(), s);
   if (st != GE_OK) return st;
   const int KB = H / 256;
   void *args[] = {&GI, &Wh, &bh, &B, &T, &GH, &R, &Z, &N, &HS, &H16, &sync};
-  return coop_launch(fwd_kernel(KB), KB - 1, H / 16, 256, (size_t)48 * H * 2, args, s, "gru recurrence (forward)");
+  return coop_launch(fwd_kernel(KB), KB - 1, H / 16 * (B / 16), fwd_lds(H), args, s, "gru recurrence (forward)");
 }
 
 int gru_rec_bwd_launch(const float *dh_out, const half_t *Wh, const float *R, const float *Z, const float *N,
                        const float *GH, const float *HS, int B, int H, int T, half_t *dGH, half_t *dGI, unsigned *sync,
                        hipStream_t s) {
-  int st = fill_zero_launch(sync, 2 * sizeof(unsigned), s);
+  int st = fill_zero_launch(sync, gru_sync_bytes(), s);
   if (st != GE_OK) return st;
   const int KB = H / 256;
   void *args[] = {&dh_out, &Wh, &R, &Z, &N, &GH, &HS, &B, &T, &dGH, &dGI, &sync};
-  const size_t lds = (size_t)16 * 3 * H * 2 + (size_t)3 * 4 * 64 * 16;
-  return coop_launch(bwd_kernel(KB), 4 + KB - 1, H / 16, 1024, lds, args, s, "gru recurrence (backward)");
+  return coop_launch(bwd_kernel(KB), 4 + KB - 1, H / 16 * (B / 16), bwd_lds(H), args, s,
+                     "gru recurrence (backward)");
 }
 
 }  // namespace ge

@@ -503,8 +503,9 @@ int gru_gates_bwd(const float *dh_out, const float *carry, const float *r, const
  * GE_GRU_STEPWISE launches a GEMM and a gate kernel per timestep (any size),
  * GE_GRU_PERSISTENT runs each direction of the recurrence as one cooperative
  * launch with the block's slice of W_h resident in LDS ([CAT] "Keep state
- * resident"); it needs B % 16 == 0, B <= 64, H % 256 == 0, H <= 1536 and
- * cooperative launch support, and returns GE_E_UNSUPPORTED otherwise.  Both
+ * resident"); it needs B % 16 == 0, B <= 64, H % 256 == 0, H <= 1024,
+ * room for all (H / 16) x (B / 16) blocks at once and cooperative launch
+ * support, and returns GE_E_UNSUPPORTED otherwise.  Both
  * compute the same quantities; only the recurrent GEMMs' summation order
  * differs. */
 #define GE_GRU_AUTO 0

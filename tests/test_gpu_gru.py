@@ -84,12 +84,14 @@ def test_gru_full_size(ge, recurrence):
     _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, f"cfg4 {recurrence}", recurrence=recurrence)
 
 
-def test_gru_persistent_small(ge):
-    """The persistent recurrence at the smallest size it takes (B 16, H 256),
-    two steps, lock-step against the oracle."""
-    V, H, B, T = 97, 256, 16, 9
+@pytest.mark.parametrize("H,B,T", [(256, 16, 9), (768, 48, 5)])
+def test_gru_persistent_small(ge, H, B, T):
+    """The persistent recurrence at the smallest size it takes (B 16, H 256:
+    one row group of 16 blocks) and at H 768, B 48 (three row groups, each
+    with a barrier of its own), two steps, lock-step against the oracle."""
+    V = 97
     p = oracle.gru_flatten(datagen.gru_params(H, V))
-    _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, "persistent small", steps=2, recurrence="persistent")
+    _run_and_check(ge, V, H, B, T, 0.01, 0.9, p, f"persistent H{H} B{B}", steps=2, recurrence="persistent")
 
 
 def test_gru_persistent_refuses_unsupported_sizes(ge):
