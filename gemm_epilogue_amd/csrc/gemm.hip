@@ -117,6 +117,8 @@ namespace {
 
 int64_t ntiles(int64_t M, int64_t N, int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); }
 int64_t t256_128(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 127) / 128); }
+// shapes the eight-wave kernel takes: whole 16-byte chunks along every dimension
+bool x8_shape(int64_t M, int64_t N, int64_t K) { return M % 8 == 0 && N % 8 == 0 && K % 8 == 0 && M >= 8 && N >= 8; }
 
 Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   Plan pl;
@@ -139,9 +141,10 @@ Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   } else if (split_k < 1 && nk >= 48 && t256 * std::min<int64_t>(nk / 8, 64) >= 192) {
     pl.bm = pl.bn = 256;
     s = (int)std::min<int64_t>({(256 + t256 - 1) / t256, nk / 8, 64});
-  } else if (split_k < 1 && t256_128(M, N) >= 192 && nk >= 24) {
-    // 256x128 on four waves: less LDS traffic per MFMA than 128x128; measured
-    // faster once the k loop is long (slower at 13 k-tiles)
+  } else if (split_k < 1 && t256_128(M, N) >= 192 && (nk >= 24 || (ab_type != GE_F32 && nk >= 12 && x8_shape(M, N, K)))) {
+    // 256x128: less operand traffic into LDS per MFMA than 128x128; on four
+    // waves measured faster once the k loop is long (slower at 13 k-tiles),
+    // on the eight-wave kernel already at 13
     pl.bm = 256;
     pl.bn = 128;
   } else if (ntiles(M, N, 128) >= 160) {
@@ -239,11 +242,12 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart) {
     gp.clamp = gp.a_vec && gp.b_vec && a.M >= v && a.N >= v && (!a_mc || a.M % v == 0) && (!b_mc || a.N % v == 0);
   }
   // the eight-wave kernel takes the plan's 256x256 or 256x128 tiles (same
-  // tiles and splits, so the same workspace) when every tile is whole, K is
-  // whole 64-wide k-tiles, the rows are 16-byte aligned and the buffer offsets
-  // of one tile stay below 2^31 bytes
+  // tiles and splits, so the same workspace) when M, N and K are multiples of
+  // 8 (edge tiles read clamped rows, the last k-tile is zero-padded), the
+  // rows are 16-byte aligned and the buffer offsets of one tile stay below
+  // 2^31 bytes
   if ((a.ab_type == GE_F16 || a.ab_type == GE_BF16) && pl.bm == 256 && (pl.bn == 256 || pl.bn == 128) &&
-      a.M % 256 == 0 && a.N % pl.bn == 0 && a.K % 64 == 0 && gp.a_vec && gp.b_vec) {
+      x8_shape(a.M, a.N, a.K) && gp.a_vec && gp.b_vec) {
     auto span = [&](bool kc, int64_t ld, int64_t w) { return kc ? ((w - 1) * ld + a.K) * es : (a.K * ld + w) * es; };
     const bool a_kc = a.layout != GE_TN, b_kc = a.layout == GE_NT;
     if (span(a_kc, a.lda, 256) < ((int64_t)1 << 31) && span(b_kc, a.ldb, pl.bn) < ((int64_t)1 << 31))

@@ -1181,8 +1181,12 @@ constexpr int X8_BK = 64;  // k per stage
 // LDS bytes of one stage (A tile 256 x 64, B tile BN x 64) and of the kernel
 // (two stages, or the FP32 staging of half the tile for the epilogue)
 template <int BN> constexpr int x8_stage() { return (256 + BN) * X8_BK * 2; }
-template <int BN> constexpr int x8_smem() {
-  return 2 * x8_stage<BN>() > 128 * (BN + 4) * 4 ? 2 * x8_stage<BN>() : 128 * (BN + 4) * 4;
+// stages in the LDS ring: three of 48 KB for 256x128 tiles, two of 64 KB for
+// 256x256; NT (both operands k-contiguous) measured faster on two
+template <int BN, int LAYOUT> constexpr int x8_nstage() { return BN == 128 && LAYOUT != GE_NT ? 3 : 2; }
+template <int BN, int LAYOUT> constexpr int x8_smem() {
+  return x8_nstage<BN, LAYOUT>() * x8_stage<BN>() > 128 * (BN + 4) * 4 ? x8_nstage<BN, LAYOUT>() * x8_stage<BN>()
+                                                                       : 128 * (BN + 4) * 4;
 }
 
 __device__ __forceinline__ int x8_kc_swz(int row) { return (row >> 1) & 7; }
@@ -1193,9 +1197,11 @@ __device__ __forceinline__ int x8_mc_swz(int k) { return 2 * (k & 3); }
 // m/n-contiguous tile W wide: its k-rows are 2 W bytes, so instruction ins
 // covers k-rows (1024 / 2W) ins .. + 1024 / 2W - 1 (two k-rows at W = 256,
 // four at W = 128).  The rest of the address is uniform and goes in the
-// scalar offset.
+// scalar offset.  wv (a multiple of 8) is how many of the tile's W rows or
+// columns lie inside the operand: on an edge tile an m/n-contiguous lane past
+// it reads the last valid 8 columns instead (those outputs are never stored).
 template <bool KC, int W>
-__device__ __forceinline__ void x8_lane_offsets(int64_t ld, int es, int lane, uint32_t (&vo)[2]) {
+__device__ __forceinline__ void x8_lane_offsets(int64_t ld, int es, int lane, int wv, uint32_t (&vo)[2]) {
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     if constexpr (KC) {
@@ -1205,23 +1211,73 @@ __device__ __forceinline__ void x8_lane_offsets(int64_t ld, int es, int lane, ui
     } else if constexpr (W == 256) {
       const int k = par * 2 + (lane >> 5);
       const int sl = ((lane & 31) >> 1) ^ x8_mc_swz(k);
-      vo[par] = (uint32_t)(((lane >> 5) * ld + 16 * sl + 8 * (lane & 1)) * es);
+      const int col = min(16 * sl + 8 * (lane & 1), wv - 8);
+      vo[par] = (uint32_t)(((lane >> 5) * ld + col) * es);
     } else {
       // four k-rows per instruction: k & 3 = lane >> 4 for every instruction
       const int kl = lane >> 4;
       const int sl = ((lane & 15) >> 1) ^ x8_mc_swz(kl);
-      vo[par] = (uint32_t)((kl * ld + 16 * sl + 8 * (lane & 1)) * es);
+      const int col = min(16 * sl + 8 * (lane & 1), wv - 8);
+      vo[par] = (uint32_t)((kl * ld + col) * es);
     }
   }
 }
 
-// base points at the tile's first row (k-contiguous) or first column (m/n-contiguous)
+// The uniform part of instruction ins's address at k-tile offset k0; on an
+// edge tile the rows of a k-contiguous operand past wv are read from its last
+// eight valid rows instead (uniform, as wv is a multiple of 8).
 template <bool KC, int W>
-__device__ __forceinline__ void x8_load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int es, int k0, char *lds_tile, int ins,
-                                        const uint32_t (&vo)[2]) {
+__device__ __forceinline__ uint32_t x8_soff(int64_t ld, int es, int k0, int ins, int wv) {
   constexpr int KPI = 1024 / (2 * W);  // k-rows per instruction of an m/n-contiguous tile
-  const uint32_t so = KC ? (uint32_t)(((int64_t)(ins * 8) * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * KPI) * ld * es);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds_tile + ins * 1024), 16, vo[ins & 1], so, 0, 0);
+  const int r0 = ins * 8 < wv - 8 ? ins * 8 : wv - 8;
+  return KC ? (uint32_t)(((int64_t)r0 * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * KPI) * ld * es);
+}
+
+// Buffer resource of an operand tile: base address, no stride, the largest
+// record count and the data-format word of a raw 32-bit buffer.
+__device__ __forceinline__ u32x4 x8_rsrc(const void *base) {
+  const uint64_t b = (uint64_t)base;
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32), 0x7fffffffu, 0x00020000u};
+}
+
+// One 16-byte-per-lane load from global memory straight into LDS (lane l's
+// bytes land at lds_tile + ins * 1024 + 16 l); base points at the tile's first
+// row (k-contiguous) or first column (m/n-contiguous).  Written as inline asm
+// because the compiler, seeing a load that writes LDS, waits for every such
+// load before the next LDS read, which would stall each k-step on the loads
+// of the following one; the kernel orders these loads with explicit waits.
+// The asm has no outputs.  The compiler does not look inside it for hazards,
+// so it opens with five wait states: the most a buffer load needs after a
+// VALU write of an SGPR it reads (readfirstlane of the scalar offset) and
+// after the SALU write of M0.
+template <bool KC, int W>
+__device__ __forceinline__ void x8_load(const u32x4 &rs, int64_t ld, int es, int k0, char *lds_tile, int ins, int wv,
+                                        const uint32_t (&vo)[2]) {
+  // both are uniform; readfirstlane keeps them in SGPRs where the compiler's
+  // divergence analysis cannot see that
+  const uint32_t so = __builtin_amdgcn_readfirstlane(x8_soff<KC, W>(ld, es, k0, ins, wv));
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(lds_tile + ins * 1024));
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vo[ins & 1]), "s"(rs), "s"(so), "{m0}"(m0v)
+               : "memory");
+}
+
+// The same 16 bytes for the last, partial k-tile (K % 64 != 0): an ordinary
+// load and LDS store, zero where the lane's k (its 8-wide chunk of a
+// k-contiguous row, or its k-row) is at or past K, so the padded products
+// add exact zeros.  The LDS slot is the lane's, as the direct load writes it.
+template <bool KC, int W>
+__device__ __forceinline__ void x8_load_tail(const char *base, int64_t ld, int es, int k0, int K, char *lds_tile,
+                                             int ins, int wv, const uint32_t (&vo)[2], int lane) {
+  constexpr int KPI = 1024 / (2 * W);
+  int k;
+  if constexpr (KC) {
+    k = k0 + 8 * ((lane & 7) ^ x8_kc_swz((ins & 1) * 8 + (lane >> 3)));
+  } else {
+    k = k0 + ins * KPI + (W == 256 ? (lane >> 5) : (lane >> 4));
+  }
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (k < K) v = *(const u32x4 *)(base + vo[ins & 1] + x8_soff<KC, W>(ld, es, k0, ins, wv));
+  *(lds_u32x4 *)(lds_tile + ins * 1024 + lane * 16) = v;
 }
 
 // fragment of the 32x32x16 MFMA: rows r .. r+31 of the operand, k block kb
@@ -1256,33 +1312,46 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
   constexpr bool B_KC = (LAYOUT == GE_NT);
   constexpr int TILE_A = BM * X8_BK * 2;
   constexpr int STAGE = x8_stage<BN>();
+  constexpr int NS = x8_nstage<BN, LAYOUT>();
   constexpr int BPW = BN / 64;  // B tile load instructions per wave
   typedef typename Mfma32<T>::V V;
-  __shared__ __attribute__((aligned(1024))) char smem[x8_smem<BN>()];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) char smem[x8_smem<BN, LAYOUT>()];
+  // the wave index is uniform; saying so keeps the loads' scalar offsets in
+  // SGPRs (otherwise each direct load sits in a loop over distinct values)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = BN == 256 ? (wave >> 2) * 128 : (wave >> 1) * 64;
   const int wn0 = BN == 256 ? (wave & 3) * 64 : (wave & 1) * 64;
   int bm0, bn0, split;
   block_work(p, BM, BN, bm0, bn0, split);
-  const int nk = p.K / X8_BK;
+  const int nk = (p.K + X8_BK - 1) / X8_BK;
+  const bool ktail = (p.K % X8_BK) != 0;  // the last k-tile is partial
+  const int mv = min(BM, p.M - bm0), nv = min(BN, p.N - bn0);  // valid rows / columns of the tile
   const int kt0 = split * p.ktiles_per_split;
   const int kt1 = min(nk, kt0 + p.ktiles_per_split);
   constexpr int es = (int)sizeof(T);
   // buffer resources based at this tile's rows / columns (offsets stay far below 2^31)
   const T *Ab = (const T *)p.A + (A_KC ? (int64_t)bm0 * p.lda : (int64_t)bm0);
   const T *Bb = (const T *)p.B + (B_KC ? (int64_t)bn0 * p.ldb : (int64_t)bn0);
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)Ab, (short)0, 0x7fffffff, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bb, (short)0, 0x7fffffff, 0x00020000);
+  const u32x4 ra = x8_rsrc(Ab), rb = x8_rsrc(Bb);
   uint32_t voa[2], vob[2];
-  x8_lane_offsets<A_KC, BM>(p.lda, es, lane, voa);
-  x8_lane_offsets<B_KC, BN>(p.ldb, es, lane, vob);
+  x8_lane_offsets<A_KC, BM>(p.lda, es, lane, mv, voa);
+  x8_lane_offsets<B_KC, BN>(p.ldb, es, lane, nv, vob);
   // a stage: 32 instructions for the A tile (4 per wave), BN / 8 for the B tile
   auto issue = [&](int t) {
-    char *st = smem + (t & 1) * STAGE;
+    char *st = smem + (t % NS) * STAGE;
+    if (ktail && t == nk - 1) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x8_load<A_KC, BM>(ra, p.lda, es, t * X8_BK, st, wave * 4 + u, voa);
+      for (int u = 0; u < 4; ++u)
+        x8_load_tail<A_KC, BM>((const char *)Ab, p.lda, es, t * X8_BK, p.K, st, wave * 4 + u, mv, voa, lane);
 #pragma unroll
-    for (int u = 0; u < BPW; ++u) x8_load<B_KC, BN>(rb, p.ldb, es, t * X8_BK, st + TILE_A, wave * BPW + u, vob);
+      for (int u = 0; u < BPW; ++u)
+        x8_load_tail<B_KC, BN>((const char *)Bb, p.ldb, es, t * X8_BK, p.K, st + TILE_A, wave * BPW + u, nv, vob, lane);
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x8_load<A_KC, BM>(ra, p.lda, es, t * X8_BK, st, wave * 4 + u, mv, voa);
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) x8_load<B_KC, BN>(rb, p.ldb, es, t * X8_BK, st + TILE_A, wave * BPW + u, nv, vob);
   };
 
   f32x16 acc[FA][2];
@@ -1322,13 +1391,19 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
   if (kt0 < kt1) issue(kt0);
+  if (NS == 3 && kt0 + 1 < kt1) issue(kt0 + 1);
   for (int t = kt0; t < kt1; ++t) {
-    // stage t's loads (the only ones in flight) and the previous stage's LDS reads are done
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    __syncthreads();
-    if (t + 1 < kt1) issue(t + 1);
+    // stage t's loads and the previous stage's LDS reads are done; in a
+    // three-stage ring stage t + 1's loads (the wave's last 4 + BPW
+    // instructions) may stay in flight
+    if (NS == 3 && t + 1 < kt1) __builtin_amdgcn_s_waitcnt(0x0070 | (4 + BPW));
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    // a bare barrier: the waits above are the ordering this needs, and a
+    // fenced barrier would also wait for the loads still in flight
+    asm volatile("s_barrier" ::: "memory");
+    if (t + NS - 1 < kt1) issue(t + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
-    const char *st = smem + (t & 1) * STAGE;
+    const char *st = smem + (t % NS) * STAGE;
     phase(st, 0, fa0, fb0, fa1, fb1, t > kt0);  // with the MFMAs of the previous stage's last block
     phase(st, 1, fa1, fb1, fa0, fb0, true);
     phase(st, 2, fa0, fb0, fa1, fb1, true);

@@ -208,7 +208,11 @@ def test_cfg1_4096_sampled(ge, layout):
 # GPU, split-K (then the finishing pass applies the epilogue) when they do not
 # 256x256 tiles for the first three; 256x128 tiles (eight waves, 64x64 each)
 # for the last two, the shapes of the 784-2048-2048-10 step's middle layer
-X8 = [(4096, 3072, 256), (3072, 4096, 512), (512, 512, 16384), (4096, 2048, 2048), (4096, 1536, 1536)]
+# whole tiles; then the step's K = 784 and M = 784 shapes (a partial last
+# k-tile, an edge row of tiles) and edge tiles along both M and N with a
+# k-tail of 8 (4120 x 3000 x 200) or of 8 in a single k-tile (1032 x 12296 x 72)
+X8 = [(4096, 3072, 256), (3072, 4096, 512), (512, 512, 16384), (4096, 2048, 2048), (4096, 1536, 1536),
+      (4096, 2048, 784), (784, 2048, 4096), (4120, 3000, 200), (1032, 12296, 72)]
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
