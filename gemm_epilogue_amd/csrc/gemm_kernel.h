@@ -1177,6 +1177,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int X8_BK = 64;  // k per stage
+template <bool B> struct BoolC { static constexpr bool value = B; };
 
 // LDS bytes of one stage (A tile 256 x 64, B tile BN x 64) and of the kernel
 // (two stages, or the FP32 staging of half the tile for the epilogue)
@@ -1390,9 +1391,9 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  if (kt0 < kt1) issue(kt0);
-  if (NS == 3 && kt0 + 1 < kt1) issue(kt0 + 1);
-  for (int t = kt0; t < kt1; ++t) {
+  // one k-step; `first` (a compile-time flag, so the steady-state loop has no
+  // branch between its LDS reads and MFMAs) skips the previous step's MFMAs
+  auto step = [&](int t, auto first) {
     // stage t's loads and the previous stage's LDS reads are done; in a
     // three-stage ring stage t + 1's loads (the wave's last 4 + BPW
     // instructions) may stay in flight
@@ -1404,11 +1405,15 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
     if (t + NS - 1 < kt1) issue(t + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
     const char *st = smem + (t % NS) * STAGE;
-    phase(st, 0, fa0, fb0, fa1, fb1, t > kt0);  // with the MFMAs of the previous stage's last block
+    phase(st, 0, fa0, fb0, fa1, fb1, !decltype(first)::value);  // with the previous stage's last MFMAs
     phase(st, 1, fa1, fb1, fa0, fb0, true);
     phase(st, 2, fa0, fb0, fa1, fb1, true);
     phase(st, 3, fa1, fb1, fa0, fb0, true);
-  }
+  };
+  if (kt0 < kt1) issue(kt0);
+  if (NS == 3 && kt0 + 1 < kt1) issue(kt0 + 1);
+  if (kt0 < kt1) step(kt0, BoolC<true>{});
+  for (int t = kt0 + 1; t < kt1; ++t) step(t, BoolC<false>{});
   if (kt0 < kt1) mma(fa1, fb1);
   __builtin_amdgcn_s_waitcnt(0x0070);
   __syncthreads();
