@@ -17,6 +17,32 @@ typedef half_t f16x8 __attribute__((ext_vector_type(8)));
 typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
 typedef half_t f16x4 __attribute__((ext_vector_type(4)));
 typedef bf16_t bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---- loads from global memory straight into LDS -------------------------------
+// Buffer resource of a raw 32-bit buffer at base: no stride, the largest record
+// count and the data-format word of a raw buffer.
+__device__ __forceinline__ u32x4 raw_buffer_rsrc(const void *base) {
+  const uint64_t b = (uint64_t)base;
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32), 0x7fffffffu, 0x00020000u};
+}
+
+// 16 bytes per lane from rs + voff (per lane) + soff (uniform) into LDS, lane
+// l's bytes at dst + 16 l (dst uniform).  Written as inline asm because the
+// compiler, seeing a load that writes LDS, waits for every such load before
+// the next LDS read, so a prefetch could never overlap the work on the data
+// already there; callers order these loads with explicit s_waitcnt vmcnt and
+// barriers.  The asm has no outputs.  The compiler does not look inside it
+// for hazards, so it opens with five wait states: the most a buffer load
+// needs after a VALU write of an SGPR it reads (the readfirstlane below) and
+// after the SALU write of M0.
+__device__ __forceinline__ void lds_dma16(const u32x4 &rs, uint32_t voff, uint32_t soff, char *dst) {
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)dst);
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(so), "{m0}"(m0v)
+               : "memory");
+}
 
 inline int dtype_size(int t) { return t == GE_F32 ? 4 : 2; }
 inline bool dtype_ok(int t) { return t == GE_F32 || t == GE_F16 || t == GE_BF16; }

@@ -331,7 +331,6 @@ template <> struct FragA<float> {
   }
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // element e of a 16-byte vector holding T values, as raw bits
@@ -1174,7 +1173,6 @@ template <> struct Mfma32<bf16_t> {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int X8_BK = 64;  // k per stage
 template <bool B> struct BoolC { static constexpr bool value = B; };
@@ -1234,32 +1232,13 @@ __device__ __forceinline__ uint32_t x8_soff(int64_t ld, int es, int k0, int ins,
   return KC ? (uint32_t)(((int64_t)r0 * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * KPI) * ld * es);
 }
 
-// Buffer resource of an operand tile: base address, no stride, the largest
-// record count and the data-format word of a raw 32-bit buffer.
-__device__ __forceinline__ u32x4 x8_rsrc(const void *base) {
-  const uint64_t b = (uint64_t)base;
-  return u32x4{(uint32_t)b, (uint32_t)(b >> 32), 0x7fffffffu, 0x00020000u};
-}
-
-// One 16-byte-per-lane load from global memory straight into LDS (lane l's
-// bytes land at lds_tile + ins * 1024 + 16 l); base points at the tile's first
-// row (k-contiguous) or first column (m/n-contiguous).  Written as inline asm
-// because the compiler, seeing a load that writes LDS, waits for every such
-// load before the next LDS read, which would stall each k-step on the loads
-// of the following one; the kernel orders these loads with explicit waits.
-// The asm has no outputs.  The compiler does not look inside it for hazards,
-// so it opens with five wait states: the most a buffer load needs after a
-// VALU write of an SGPR it reads (readfirstlane of the scalar offset) and
-// after the SALU write of M0.
+// One 16-byte-per-lane load of instruction ins into LDS (lane l's bytes land
+// at lds_tile + ins * 1024 + 16 l); base points at the tile's first row
+// (k-contiguous) or first column (m/n-contiguous).
 template <bool KC, int W>
 __device__ __forceinline__ void x8_load(const u32x4 &rs, int64_t ld, int es, int k0, char *lds_tile, int ins, int wv,
                                         const uint32_t (&vo)[2]) {
-  // both are uniform; readfirstlane keeps them in SGPRs where the compiler's
-  // divergence analysis cannot see that
-  const uint32_t so = __builtin_amdgcn_readfirstlane(x8_soff<KC, W>(ld, es, k0, ins, wv));
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)(lds_tile + ins * 1024));
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(vo[ins & 1]), "s"(rs), "s"(so), "{m0}"(m0v)
-               : "memory");
+  lds_dma16(rs, vo[ins & 1], x8_soff<KC, W>(ld, es, k0, ins, wv), lds_tile + ins * 1024);
 }
 
 // The same 16 bytes for the last, partial k-tile (K % 64 != 0): an ordinary
@@ -1333,7 +1312,7 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
   // buffer resources based at this tile's rows / columns (offsets stay far below 2^31)
   const T *Ab = (const T *)p.A + (A_KC ? (int64_t)bm0 * p.lda : (int64_t)bm0);
   const T *Bb = (const T *)p.B + (B_KC ? (int64_t)bn0 * p.ldb : (int64_t)bn0);
-  const u32x4 ra = x8_rsrc(Ab), rb = x8_rsrc(Bb);
+  const u32x4 ra = raw_buffer_rsrc(Ab), rb = raw_buffer_rsrc(Bb);
   uint32_t voa[2], vob[2];
   x8_lane_offsets<A_KC, BM>(p.lda, es, lane, mv, voa);
   x8_lane_offsets<B_KC, BN>(p.ldb, es, lane, nv, vob);

@@ -46,7 +46,6 @@ typedef uint32_t mk_u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) mk_u32x4 lds_mk_u32x4;
 typedef uint32_t mk_u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) mk_u32x2 lds_mk_u32x2;
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int MD = 512;       // model width the kernel is built for
 constexpr int MC = 64;        // hidden units per chunk
@@ -115,7 +114,7 @@ __global__ __launch_bounds__(256, 1) void mlp_block_fused_kernel(const T *__rest
   typedef typename MkMfma<T>::V V;
   __shared__ __attribute__((aligned(1024))) char smem[WU_BYTES + WD_BYTES + AS_BYTES];
   char *const Wu = smem, *const Wd = smem + WU_BYTES, *const As = smem + WU_BYTES + WD_BYTES;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = wave & 1, eh = wave >> 1;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t b0 = (int64_t)blockIdx.x * MBR;
@@ -126,15 +125,14 @@ __global__ __launch_bounds__(256, 1) void mlp_block_fused_kernel(const T *__rest
   // ---- weight slices: buffer loads that write LDS ---------------------------
   // a wave's load instruction fills 1 KB of LDS, lane i the 16 bytes at i * 16;
   // a slice is 64 such instructions, 16 per wave
-  const __amdgpu_buffer_rsrc_t rwu = __builtin_amdgcn_make_buffer_rsrc((void *)wut, (short)0, 0x7fffffff, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rwd = __builtin_amdgcn_make_buffer_rsrc((void *)wdt, (short)0, 0x7fffffff, 0x00020000);
+  const u32x4 rwu = raw_buffer_rsrc(wut), rwd = raw_buffer_rsrc(wdt);
   auto issue_wu = [&](int c) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int ins = wave * 16 + j, p = ins * 64 + lane;  // LDS chunk position this lane fills
       const int rr = p >> 6, cc = swz_wu(rr, p & 63);
       const uint32_t vo = (uint32_t)(((int64_t)(c * MC + rr) * MD + cc * 8) * (int64_t)sizeof(T));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rwu, (lds_void_t *)(Wu + ins * 1024), 16, vo, 0, 0, 0);
+      lds_dma16(rwu, vo, 0, Wu + ins * 1024);
     }
   };
   auto issue_wd = [&](int c) {
@@ -143,7 +141,7 @@ __global__ __launch_bounds__(256, 1) void mlp_block_fused_kernel(const T *__rest
       const int ins = wave * 16 + j, p = ins * 64 + lane;
       const int e = p >> 3, cc = swz_128(e, p & 7);
       const uint32_t vo = (uint32_t)(((int64_t)e * F + c * MC + cc * 8) * (int64_t)sizeof(T));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rwd, (lds_void_t *)(Wd + ins * 1024), 16, vo, 0, 0, 0);
+      lds_dma16(rwd, vo, 0, Wd + ins * 1024);
     }
   };
   issue_wu(0);
