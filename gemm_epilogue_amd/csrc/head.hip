@@ -12,11 +12,12 @@
 //
 // A prep kernel writes W (D x C, row-major) in the two layouts the MFMAs
 // read, zero-padded to 16 classes: W^T (16 x D) and W (D x 16), 128 KiB for
-// D = 2048, which stay in L2.  A block of four waves takes 16 rows and splits
-// D four ways: each wave accumulates its quarter of the logits, the quarters
-// are added through LDS in wave order (so every wave holds the same logits
-// and computes the same loss and G), and each wave then forms dH for its own
-// quarter of the hidden units.  H is read once.
+// D = 2048, which stay in L2.  A block of NW waves (eight when D is a
+// multiple of 256, else four) takes 16 rows and splits D NW ways: each wave
+// accumulates its share of the logits, the shares are added through LDS in
+// wave order (so every wave holds the same logits and computes the same loss
+// and G), and each wave then forms dH for its own share of the hidden units.
+// H is read once; eight waves keep twice the loads in flight per CU.
 //  * Z: v_mfma_f32_16x16x32_f16 over D in chunks of 32, the W^T fragment in
 //    the first operand slot, so lane l owns Z[row l%16][4(l/16) .. +3].
 //  * loss and G: the four lanes of a row (l, l^16, l^32, l^48) reduce the
@@ -36,9 +37,9 @@ namespace ge {
 
 namespace {
 
-constexpr int HEAD_ROWS = 16;   // rows per block (four waves splitting D)
+constexpr int HEAD_ROWS = 16;   // rows per block (its waves splitting D)
 constexpr int HEAD_PART = 17;   // floats per block partial: 16 column sums + loss sum
-constexpr int HEAD_DMAX = 2048; // widest input (a wave keeps the ReLU mask of its quarter in 4 registers)
+constexpr int HEAD_DMAX = 2048; // widest input (a wave keeps the ReLU mask of its share in registers)
 
 typedef uint32_t hu32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t hu32x4 __attribute__((ext_vector_type(4)));
@@ -60,18 +61,25 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 }  // namespace
 
-// W (D x C) -> WT (16 x D) and WP (D x 16), classes C..15 zero
+// W (D x C) -> WT (16 x D) and WP (D x 16), classes C..15 zero.  Thread i
+// writes element i of each layout, so both stores are consecutive across
+// the threads; the reads of W (40 KB at D = 2048) gather from L2.
 __global__ __launch_bounds__(256) void mlp_head_prep_kernel(const half_t *__restrict__ W, int D, int C,
                                                             half_t *__restrict__ WT, half_t *__restrict__ WP) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= D * 16) return;
-  const int k = i >> 4, c = i & 15;
-  const half_t v = c < C ? W[(int64_t)k * C + c] : (half_t)0.f;
-  WP[i] = v;
-  WT[(int64_t)c * D + k] = v;
+  {
+    const int k = i >> 4, c = i & 15;  // WP[k][c]
+    WP[i] = c < C ? W[(int64_t)k * C + c] : (half_t)0.f;
+  }
+  {
+    const int c = i / D, k = i - c * D;  // WT[c][k]
+    WT[i] = c < C ? W[(int64_t)k * C + c] : (half_t)0.f;
+  }
 }
 
-__global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict__ H, int B, int D,
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void mlp_head_kernel(const half_t *__restrict__ H, int B, int D,
                                                       const half_t *__restrict__ WT,
                                                       const half_t *__restrict__ WP, const float *__restrict__ bias,
                                                       int C, const int32_t *__restrict__ labels, float gscale,
@@ -80,20 +88,20 @@ __global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict_
                                                       float *__restrict__ part, float *__restrict__ dpart) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
-  __shared__ f32x4 red[4][64];
+  __shared__ f32x4 red[NW][64];
 
   const int row = blockIdx.x * HEAD_ROWS + r16;
   const bool rok = row < B;
   const half_t *hrow = H + (int64_t)min(row, B - 1) * D;
 
   // ---- Z = H W (FP32 accumulation), lane: row r16, classes 4q .. 4q+3.
-  // Wave w takes chunks w*nch .. (w+1)*nch - 1 of 32 units.  In each chunk
+  // Wave w takes chunks w*nch .. (w+1)*nch - 1 of 32 units (nch = D / (32 NW)).  In each chunk
   // lane q supplies units 8q .. 8q+7 -- the units it owns in dH below -- so
   // the ReLU mask [H > 0] is kept here as bits (8 per chunk).  The wave's
   // chunks are loaded 8 at a time, two batches in flight; the loops are
   // unrolled over the widest D so the mask bits stay in registers.
-  constexpr int NCH = HEAD_DMAX / 128;  // chunks per wave at the widest D
-  const int nch = D / 128;
+  constexpr int NCH = HEAD_DMAX / (32 * NW);  // chunks per wave at the widest D
+  const int nch = D / (32 * NW);
   const int cbase = wave * nch;
   uint32_t mb[NCH / 4];
 #pragma unroll
@@ -141,10 +149,12 @@ __global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict_
       }
     }
   }
-  // the four quarters, added in wave order
+  // the NW shares, added in wave order
   red[wave][lane] = acc;
   __syncthreads();
-  acc = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  acc = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) acc += red[w][lane];
 
   // ---- stable softmax cross-entropy of the row, shared by its four lanes
   float z[4];
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict_
     if (q == 0) row_loss[row] = rl;
   }
 
-  // ---- block partials: column sums of G over the 16 rows, sum of row losses
+  // ---- block partials: column sums of G over the block's rows, sum of row losses
   {
     float lsum = (rok && q == 0) ? rl : 0.f;
 #pragma unroll
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(256) void mlp_head_kernel(const half_t *__restrict_
             o[4 + t] = (half_t)(((bits >> (4 + t)) & 1u) ? d1[t] : 0.f);
           }
           if (rok) *(f16x8 *)(drow + 32 * c) = o;
-          // column sums of the stored dH over the block's 16 rows (the bias
+          // column sums of the stored dH over the block's rows (the bias
           // gradient of the layer below), a fixed butterfly over the rows
           float cs[8];
 #pragma unroll
@@ -377,8 +387,12 @@ int head_launch(const half_t *H, int64_t B, int64_t D, const half_t *W, const fl
                      (int)C, WT, WP);
   int s = launch_status("mlp head (prep)");
   if (s != GE_OK) return s;
-  hipLaunchKernelGGL(mlp_head_kernel, dim3(nblocks), dim3(256), 0, st, H, (int)B, (int)D, (const half_t *)WT,
-                     (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part, dpart);
+  if (D % 256 == 0)
+    hipLaunchKernelGGL(mlp_head_kernel<8>, dim3(nblocks), dim3(512), 0, st, H, (int)B, (int)D, (const half_t *)WT,
+                       (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part, dpart);
+  else
+    hipLaunchKernelGGL(mlp_head_kernel<4>, dim3(nblocks), dim3(256), 0, st, H, (int)B, (int)D, (const half_t *)WT,
+                       (const half_t *)WP, bias, (int)C, labels, gscale, Z, G, row_loss, dH, part, dpart);
   s = launch_status("mlp head");
   if (s != GE_OK) return s;
   hipLaunchKernelGGL(mlp_head_final_kernel, dim3((unsigned)(1 + (D + 63) / 64)), dim3(HEAD_PART * 32), 0, st,

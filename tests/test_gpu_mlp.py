@@ -241,6 +241,22 @@ def test_mlp_hidden_bias_from_dgrad_partials(ge):
         _check_step(tr, dims, X, y, 0.1, 0.9, "f32", w0, v0, 1e-6, f"784-512-256-10 step {step}")
 
 
+@pytest.mark.parametrize("hidden", [384, 512])
+def test_head_block_widths_lockstep(ge, hidden):
+    """The fused output layer with four waves per block (D = 384, not a
+    multiple of 256) and eight (D = 512), FP16 storage, a batch of 200 (a
+    partial last block of 16 rows), two steps lock-step against the oracle."""
+    dims = [784, hidden, 10]
+    B, lr, mu = 200, 0.05, 0.9
+    p0 = datagen.he_uniform_flat(dims)
+    tr = ge.MLPTrainer(dims, B, torch.float16, params=torch.from_numpy(p0).float().cuda())
+    for step in range(2):
+        X, y = datagen.template_images(B, 31, fmt="f16", batch=step)
+        w0, v0 = host(tr.params), host(tr.velocity)
+        tr.step(torch.from_numpy(X).half().cuda(), torch.from_numpy(y).cuda(), lr, mu)
+        _check_step(tr, dims, X, y, lr, mu, "f16", w0, v0, 1e-5, f"784-{hidden}-10 step {step}")
+
+
 def test_mlp_step_deterministic(ge):
     dims = [784, 512, 512, 10]
     X, y = datagen.template_images(1000, 9, fmt="f16")
