@@ -68,6 +68,10 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
   const int ug = blockIdx.x % nug, rg = blockIdx.x / nug;
   const int u0 = ug * 16;
   unsigned *count = sync + kSyncStride * rg, *err = sync + 4 * kSyncStride;
+  // a barrier that gives up (it also sets the error word) turns every later
+  // hidden state this block writes into NaN, so the step's loss shows it;
+  // later barriers see the error word and return at once
+  bool dead = false;
   // W_h columns of this block, transposed into LDS: thread takes (k, gate),
   // reads the 16 units of row k of that gate block and writes them to 16 rows
   for (int p = tid; p < H * 3; p += 256) {
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
         r[q] = sigm(gi[0][q] + gh[0][q]);
         z[q] = sigm(gi[1][q] + gh[1][q]);
         nn[q] = tanhf(gi[2][q] + r[q] * gh[2][q]);
-        hv[q] = (1.f - z[q]) * nn[q] + z[q] * hp[q];
+        hv[q] = dead ? NAN : (1.f - z[q]) * nn[q] + z[q] * hp[q];
       }
       const int64_t o = row * H + u0 + j0;
       *(f32x4 *)(R + o) = r;
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
         for (int g = 0; g < 3; ++g) gi[g] = *(const f32x4 *)(GI + (row + B) * H3 + g * H + u0 + j0);
       }
     }
-    if (t + 1 < T && !grid_barrier(count, (unsigned)((t + 1) * nug), err)) return;
+    if (t + 1 < T && !grid_barrier(count, (unsigned)((t + 1) * nug), err)) dead = true;
   }
 }
 
@@ -174,6 +178,7 @@ __global__ __launch_bounds__(256, 1) void gru_rec_bwd_kernel(const float *__rest
   const int m = rg * 16 + (lane & 15);
   const int j0 = 4 * (lane >> 4);
   const bool gate = wave == 0;  // the wave that runs the gate backward and owns the carry
+  bool dead = false;            // as in the forward: NaN gradients after a barrier that gave up
   f32x4 carry = {0.f, 0.f, 0.f, 0.f};
   f32x4 dho, r, z, nn, ghn, h0;
   auto fetch = [&](int t) {
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(256, 1) void gru_rec_bwd_kernel(const float *__rest
       f16x4 gr, gz, gn, gnh;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float dh = dho[q] + carry[q];
+        const float dh = dead ? NAN : dho[q] + carry[q];
         const float dn = dh * (1.f - z[q]);
         const float dz = dh * (h0[q] - nn[q]);
         const float dnh = dn * (1.f - nn[q] * nn[q]);
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void gru_rec_bwd_kernel(const float *__rest
     }
     if (t == 0) break;
     ++nbar;
-    if (!grid_barrier(count, (unsigned)(nbar * nug), err)) return;
+    if (!grid_barrier(count, (unsigned)(nbar * nug), err)) dead = true;
     // carry for step t-1: dh z + dGH_t[m, :] W_h[u0 + j, :]^T over the 3H
     // columns; wave `wave` takes chunks wave KC/4 .. (wave + 1) KC/4
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
