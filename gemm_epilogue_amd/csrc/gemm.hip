@@ -128,10 +128,12 @@ Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   const int64_t t256 = ntiles(M, N, 256);
   int s = 0;  // 0: chosen below with the tile
   // The 256x256 tile is the most efficient per k-step.  Use it when the
-  // output alone gives most of the 256 CUs a tile, or when K is long enough
-  // that splitting it (at least 8 k-tiles per split) fills the CUs: measured
-  // on weight-gradient shapes (K = batch 4096), the split-K partial traffic
-  // costs less than running smaller, slower tiles.
+  // output alone gives most of the 256 CUs a tile.  When K is long enough
+  // that splitting it (at least 8 k-tiles per split) fills the CUs, split
+  // 256x128 tiles: measured on the weight-gradient shapes (K = batch 4096),
+  // half the splits' FP32 partial traffic outweighs the larger tile's
+  // cheaper k-steps (2048x2048: 51.8 against 53.3 us with the finishing
+  // pass; 784x2048: 33.4 against 35.4 us).
   if (N <= 16 && M > 16) {
     // one narrow column of tiles; split-K supplies the parallelism
     pl.bm = 128;
@@ -139,8 +141,10 @@ Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
   } else if (t256 >= 192) {
     pl.bm = pl.bn = 256;
   } else if (split_k < 1 && nk >= 48 && t256 * std::min<int64_t>(nk / 8, 64) >= 192) {
-    pl.bm = pl.bn = 256;
-    s = (int)std::min<int64_t>({(256 + t256 - 1) / t256, nk / 8, 64});
+    pl.bm = 256;
+    pl.bn = 128;
+    const int64_t t = t256_128(M, N);
+    s = (int)std::min<int64_t>({(256 + t - 1) / t, nk / 8, 64});
   } else if (split_k < 1 && t256_128(M, N) >= 192 && (nk >= 24 || (ab_type != GE_F32 && nk >= 12 && x8_shape(M, N, K)))) {
     // 256x128: less operand traffic into LDS per MFMA than 128x128; on four
     // waves measured faster once the k loop is long (slower at 13 k-tiles),
