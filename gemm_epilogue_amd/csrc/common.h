@@ -18,6 +18,7 @@ typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
 typedef half_t f16x4 __attribute__((ext_vector_type(4)));
 typedef bf16_t bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // ---- loads from global memory straight into LDS -------------------------------
@@ -38,9 +39,13 @@ __device__ __forceinline__ u32x4 raw_buffer_rsrc(const void *base) {
 // needs after a VALU write of an SGPR it reads (the readfirstlane below) and
 // after the SALU write of M0.
 __device__ __forceinline__ void lds_dma16(const u32x4 &rs, uint32_t voff, uint32_t soff, char *dst) {
+  // all uniform; readfirstlane keeps them in SGPRs where the compiler would
+  // otherwise leave a copy in VGPRs
+  const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane(rs[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rs[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(rs[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rs[3])};
   const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)dst);
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(so), "{m0}"(m0v)
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(so), "{m0}"(m0v)
                : "memory");
 }
 
