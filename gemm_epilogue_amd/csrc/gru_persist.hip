@@ -5,32 +5,33 @@
 // section "Keep state resident"; the tiny serialized per-timestep jobs are
 // the cost that section and "Why This Belongs in a Game Engine" point at).
 //
-// Block (g, q) of the (H / 16) x (B / 16) blocks owns hidden units
-// u0 = 16 g .. u0 + 15 for batch rows 16 q .. 16 q + 15; a row group q is an
+// Forward: block g of the H / 16 blocks owns hidden units u0 = 16 g .. u0 + 15
+// for all B rows; wave w takes batch rows 16 w .. 16 w + 15.
+//   step t: GH[rows, g' H + u0 + j] = h16_{t-1}[rows] W_h[:, g' H + u0 + j] + b_h
+//           for the three gate blocks g' (r, z, n) and j < 16 -- a [16 x H] x
+//           [H x 48] product per wave on MFMA with the 48 columns of W_h in
+//           LDS -- then the gate arithmetic, the stores of r, z, n, h, the FP16
+//           copy of h and GH, and one grid barrier (every block needs all of
+//           h16_t next).  A lane's h_{t-1} is its own previous output
+//           (registers), the next step's GI is fetched before the barrier, and
+//           a wave issues all of its h16 loads before its first MFMA.
+// Backward: block (g, q) of the (H / 16) x (B / 16) blocks owns units u0 =
+// 16 g .. u0 + 15 for batch rows 16 q .. 16 q + 15; a row group q is an
 // independent recurrence, so its H / 16 blocks meet at a barrier of their own.
-//   forward step t:  GH[rows, g' H + u0 + j] = h16_{t-1}[rows] W_h[:, g' H + u0 + j]
-//                    + b_h for the three gate blocks g' (r, z, n) and j < 16 --
-//                    a [16 x H] x [H x 48] product on MFMA with the 48 columns
-//                    of W_h in LDS, its H split over the block's four waves and
-//                    the partial sums added in LDS in wave order -- then the
-//                    gate arithmetic, the stores of r, z, n, h, the FP16 copy
-//                    of h and GH, and the row group's barrier (each of its
-//                    blocks needs all of h16_t for those rows next).  The
-//                    lane's h_{t-1} is its own previous output (registers),
-//                    the next step's GI is fetched before the barrier, and a
-//                    wave issues all of its h16 loads before its first MFMA.
-//   backward step t: dh = dh_out + carry for the block's units and rows (the
-//                    carry stays in registers), the gate backward, the stores
-//                    of dGH, dGI, the row group's barrier, then carry = dh z +
-//                    dGH_t[rows] W_h[u0 + j, :]^T, a [16 x 3H] x [3H x 16]
-//                    product with the 16 rows of W_h in LDS, 3H split over
-//                    the four waves and summed in LDS in wave order.
-// Splitting the batch over blocks keeps each CU's per-step h16 (or dGH)
-// traffic to its own 16 rows.  B <= 64 and B % 16 == 0; H = 256 KB for
-// KB = 1 .. 4, so the W_h slice fits LDS and a lane's loads of one step fit
-// its registers.  The gate arithmetic and every stored tensor are those of
-// gru_fwd_kernel / gru_bwd_kernel (seq.hip); only the GEMM's summation order
-// differs.
+//   step t: dh = dh_out + carry for the block's units and rows (the carry
+//           stays in registers), the gate backward, the stores of dGH, dGI,
+//           the row group's barrier, then carry = dh z + dGH_t[rows]
+//           W_h[u0 + j, :]^T, a [16 x 3H] x [3H x 16] product with the 16 rows
+//           of W_h in LDS, 3H split over the block's four waves and summed in
+//           LDS in wave order.
+// The two layouts are the measured better ones for each direction: splitting
+// the forward by row group as well (256 blocks, K split over the waves) made
+// a step 12.3 us instead of 11.4 (its barrier fences scale with the block
+// count), while the backward went from 16.6 us (64 blocks of 1,024 threads)
+// to 12.5.  B <= 64 and B % 16 == 0; H = 256 KB for KB = 1 .. 4, so the W_h
+// slice fits LDS and a lane's loads of one step fit its registers.  The gate
+// arithmetic and every stored tensor are those of gru_fwd_kernel /
+// gru_bwd_kernel (seq.hip); only the GEMM's summation order differs.
 #include "common.h"
 #include "persist.h"
 
@@ -59,15 +60,12 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
                                                              float *__restrict__ Z, float *__restrict__ Nn,
                                                              float *__restrict__ HS, half_t *__restrict__ H16,
                                                              unsigned *__restrict__ sync) {
-  constexpr int H = 256 * KB, H3 = 3 * H, NS = 2 * KB;  // 32-wide k chunks per wave
+  constexpr int H = 256 * KB, H3 = 3 * H;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  half_t *w = (half_t *)smem;                   // [48][H]: row c = gate c / 16, unit c % 16; chunks swizzled
-  f32x4 *red = (f32x4 *)(smem + 48 * H * 2);    // [3 waves][3 gates][64]
+  half_t *w = (half_t *)smem;  // [48][H]: row c = gate c / 16, unit c % 16; k contiguous, chunks swizzled
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nug = H / 16;
-  const int ug = blockIdx.x % nug, rg = blockIdx.x / nug;
-  const int u0 = ug * 16;
-  unsigned *count = sync + kSyncStride * rg, *err = sync + 4 * kSyncStride;
+  const int u0 = blockIdx.x * 16;
+  unsigned *count = sync, *err = sync + 4 * kSyncStride;
   // a barrier that gives up (it also sets the error word) turns every later
   // hidden state this block writes into NaN, so the step's loss shows it;
   // later barriers see the error word and return at once
@@ -84,51 +82,43 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
       w[row * H + swz(row, k >> 3) * 8 + (k & 7)] = u < 8 ? a[u] : b[u - 8];
     }
   }
-  const int m = rg * 16 + (lane & 15);  // batch row of this lane
-  const int j0 = 4 * (lane >> 4);       // its four units within the block
-  const int k0 = wave * (H / 4);        // this wave's quarter of the contraction
+  const int m = wave * 16 + (lane & 15);  // batch row of this lane
+  const int j0 = 4 * (lane >> 4);         // its four units within the block
+  const bool live = wave * 16 < B;
   f32x4 bias[3], gi[3];
-  f32x4 hp = {0.f, 0.f, 0.f, 0.f};  // h_{t-1} of the lane's (row, units), wave 0
+  f32x4 hp = {0.f, 0.f, 0.f, 0.f};  // h_{t-1} of the lane's (row, units)
 #pragma unroll
   for (int g = 0; g < 3; ++g) bias[g] = *(const f32x4 *)(bh + g * H + u0 + j0);
-  if (wave == 0) {
+  if (live) {
 #pragma unroll
     for (int g = 0; g < 3; ++g) gi[g] = *(const f32x4 *)(GI + (int64_t)m * H3 + g * H + u0 + j0);
   }
   __syncthreads();
   for (int t = 0; t < T; ++t) {
-    f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if (t > 0) {
-      // h16_{t-1} row m over this wave's quarter: the lane's 8 k of each 32-wide chunk
-      const half_t *hrow = H16 + ((int64_t)t * B + m) * H + k0 + 8 * (lane >> 4);
-      f16x8 hv[NS];
+    if (live) {
+      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      if (t > 0) {
+        // h16_{t-1} row m: the lane's 8 k values of each 32-wide chunk
+        const half_t *hrow = H16 + ((int64_t)t * B + m) * H + 8 * (lane >> 4);
+        f16x8 hv[8 * KB];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) hv[s] = *(const f16x8 *)(hrow + 32 * s);
+        for (int s = 0; s < 8 * KB; ++s) hv[s] = *(const f16x8 *)(hrow + 32 * s);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int c = (k0 + 32 * s) / 8 + (lane >> 4);
+        for (int s = 0; s < 8 * KB; ++s) {
+          const int c = 4 * s + (lane >> 4);
 #pragma unroll
-        for (int g = 0; g < 3; ++g) {
-          const int row = g * 16 + (lane & 15);
-          const f16x8 wv = *(const lds_f16x8_t *)(w + row * H + swz(row, c) * 8);
-          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, hv[s], acc[g], 0, 0, 0);
+          for (int g = 0; g < 3; ++g) {
+            const int row = g * 16 + (lane & 15);
+            const f16x8 wv = *(const lds_f16x8_t *)(w + row * H + swz(row, c) * 8);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, hv[s], acc[g], 0, 0, 0);
+          }
         }
       }
-      if (wave > 0) {
-#pragma unroll
-        for (int g = 0; g < 3; ++g) red[((wave - 1) * 3 + g) * 64 + lane] = acc[g];
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
       // lane holds GH[m][g H + u0 + j0 .. +3] (before the bias)
       const int64_t row = (int64_t)t * B + m;
       f32x4 gh[3], r, z, nn, hv;
 #pragma unroll
-      for (int g = 0; g < 3; ++g) {
-        if (t > 0) acc[g] = ((acc[g] + red[g * 64 + lane]) + red[(3 + g) * 64 + lane]) + red[(6 + g) * 64 + lane];
-        gh[g] = acc[g] + bias[g];
-      }
+      for (int g = 0; g < 3; ++g) gh[g] = acc[g] + bias[g];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         r[q] = sigm(gi[0][q] + gh[0][q]);
@@ -150,7 +140,7 @@ __global__ __launch_bounds__(256, 1) void gru_rec_fwd_kernel(const float *__rest
         for (int g = 0; g < 3; ++g) gi[g] = *(const f32x4 *)(GI + (row + B) * H3 + g * H + u0 + j0);
       }
     }
-    if (t + 1 < T && !grid_barrier(count, (unsigned)((t + 1) * nug), err)) dead = true;
+    if (t + 1 < T && !grid_barrier(count, (unsigned)((t + 1) * gridDim.x), err)) dead = true;
   }
 }
 
@@ -268,7 +258,7 @@ const void *bwd_kernel(int KB) {
   }
 }
 
-size_t fwd_lds(int H) { return (size_t)48 * H * 2 + (size_t)9 * 64 * 16; }
+size_t fwd_lds(int H) { return (size_t)48 * H * 2; }
 size_t bwd_lds(int H) { return (size_t)16 * 3 * H * 2 + (size_t)3 * 64 * 16; }
 
 // the dynamic LDS above the default limit has to be granted per kernel
@@ -308,9 +298,10 @@ bool gru_persist_supported(int64_t B, int64_t H) {
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
   // every block of either kernel must be resident at once
-  const int KB = (int)(H / 256), blocks = (int)(H / 16 * (B / 16));
+  const int KB = (int)(H / 256);
   const void *fns[2] = {fwd_kernel(KB), bwd_kernel(KB)};
   const size_t lds[2] = {fwd_lds((int)H), bwd_lds((int)H)};
+  const int64_t blocks[2] = {H / 16, H / 16 * (B / 16)};
   for (int i = 0; i < 2; ++i) {
     int per_cu = 0;
     if (!grant(fns[i], i * 4 + KB - 1, lds[i]) ||
@@ -318,7 +309,7 @@ bool gru_persist_supported(int64_t B, int64_t H) {
       (void)hipGetLastError();
       return false;
     }
-    if ((int64_t)per_cu * cus < blocks) return false;
+    if ((int64_t)per_cu * cus < blocks[i]) return false;
   }
   return true;
 }
@@ -333,7 +324,7 @@ int gru_rec_fwd_launch(const float *GI, const half_t *Wh, const float *bh, int B
   if (st != GE_OK) return st;
   const int KB = H / 256;
   void *args[] = {&GI, &Wh, &bh, &B, &T, &GH, &R, &Z, &N, &HS, &H16, &sync};
-  return coop_launch(fwd_kernel(KB), KB - 1, H / 16 * (B / 16), fwd_lds(H), args, s, "gru recurrence (forward)");
+  return coop_launch(fwd_kernel(KB), KB - 1, H / 16, fwd_lds(H), args, s, "gru recurrence (forward)");
 }
 
 int gru_rec_bwd_launch(const float *dh_out, const half_t *Wh, const float *R, const float *Z, const float *N,
