@@ -12,6 +12,7 @@
 // per layer a TN weight-gradient GEMM and a column sum, L-1 masked NT dgrad
 // GEMMs, one update (plus a finishing pass for each split-K GEMM).
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -25,7 +26,7 @@ inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; 
 
 struct MlpLayout {
   std::vector<int64_t> h_off;  // H_1..H_{L-1}
-  int64_t z_off, g_off, dh_off[2], loss_off, gemm_ws_off, gemm_ws, cs_ws_off, cs_ws, sync_off, total;
+  int64_t z_off, g_off, dh_off[2], loss_off, gemm_ws_off, gemm_ws, gemm_ws2_off, cs_ws_off, cs_ws, sync_off, total;
   bool head;  // the last layer runs as one fused kernel (mlp_head_kernel)
   int64_t head_off;
 };
@@ -85,16 +86,54 @@ MlpLayout layout_of(const ge_mlp_desc *d, int64_t B) {
   L.gemm_ws_off = off;
   L.gemm_ws = gws;
   off = align_up(off + gws);
+  // the weight-gradient GEMMs that run beside the dgrad chain (with the fused
+  // output layer) need split-K scratch of their own
+  L.head = use_head(d, B);
+  L.gemm_ws2_off = off;
+  if (L.head) off = align_up(off + gws);
   L.cs_ws_off = off;
   L.cs_ws = cws;
   off = align_up(off + cws);
-  L.head = use_head(d, B);
   L.head_off = off;
   if (L.head) off = align_up(off + head_ws_bytes(B, d->dims[d->n_layers - 1]));
   L.sync_off = off;  // barrier counter and error word of the persistent step
   off = align_up(off + 8);
   L.total = off;
   return L;
+}
+
+// A second stream of the current device (default priority, non-blocking) and
+// two events for forking work onto it and joining back, created once per
+// device and kept for the process.
+int side_stream(hipStream_t *s2, hipEvent_t *fork, hipEvent_t *join) {
+  static std::mutex mu;
+  static hipStream_t streams[64];
+  static hipEvent_t forks[64], joins[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    set_error("mlp_train_step: no current device for the side stream");
+    return GE_E_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    hipStream_t st = nullptr;
+    hipEvent_t ef = nullptr, ej = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ef, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ej, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      set_error("mlp_train_step: cannot create the side stream or its events");
+      return GE_E_LAUNCH;
+    }
+    streams[dev] = st;
+    forks[dev] = ef;
+    joins[dev] = ej;
+  }
+  *s2 = streams[dev];
+  *fork = forks[dev];
+  *join = joins[dev];
+  return GE_OK;
 }
 
 ge_gemm_args gemm_args(int layout, int t, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
@@ -257,7 +296,26 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   } else {
     RUN(xent_launch(Z, B, d[nl], d[nl], labels, gscale, loss_out, row_loss, G, d[nl], st, nullptr, s));
   }
-  // backward
+  // backward.  With the fused output layer the weight gradients of layers
+  // L .. 2 (and their split-K finishing passes) run on a second stream
+  // beside the dgrad chain and the first layer's weight gradient: each waits
+  // for the event recorded when its dZ is complete, and the momentum update
+  // waits for the second stream.  Both orders compute the same values; the
+  // memory-bound passes of one stream fill in beside the other's GEMMs.  Not
+  // under stream capture, where the step stays on the caller's stream.
+  hipStream_t s2 = s;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  bool fork = L.head;
+  if (fork) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+      (void)hipGetLastError();
+      cs = hipStreamCaptureStatusActive;
+    }
+    fork = cs == hipStreamCaptureStatusNone;
+  }
+  if (fork) RUN(side_stream(&s2, &ev_fork, &ev_join));
+  void *gws2 = fork && L.gemm_ws ? ws + L.gemm_ws2_off : gws;
   const void *Gl = G;
   int ping = 0;
   int64_t gl_rows = 0;  // > 0: the GEMM that wrote Gl left its column partials in cws
@@ -266,9 +324,17 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
     ge_gemm_args a = gemm_args(GE_TN, st, d[l - 1], d[l], B, hptr(l - 1), d[l - 1], Gl, d[l],
                                buf->grads + w_off[l], d[l], GE_F32);
     a.alpha = alpha;
-    a.workspace = gws;
+    const bool side = fork && l >= 2;
+    a.workspace = side ? gws2 : gws;
     a.workspace_bytes = L.gemm_ws;
-    RUN(gemm_launch(a, s));
+    if (side) {
+      if (hipEventRecord(ev_fork, s) != hipSuccess || hipStreamWaitEvent(s2, ev_fork, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        set_error("mlp_train_step: cannot fork onto the side stream");
+        return GE_E_LAUNCH;
+      }
+    }
+    RUN(gemm_launch(a, side ? s2 : s));
     const bool fused = L.head && l == nl;  // db and dH of this layer came from the head
     // the head also summed the columns of dH_{L-1}, the bias gradient of layer L-1
     if (!(L.head && l >= nl - 1)) {
@@ -305,6 +371,13 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
     }
   }
   (void)es;
+  if (fork) {
+    if (hipEventRecord(ev_join, s2) != hipSuccess || hipStreamWaitEvent(s, ev_join, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      set_error("mlp_train_step: cannot join the side stream");
+      return GE_E_LAUNCH;
+    }
+  }
   return sgd_launch(buf->params, buf->grads, buf->velocity, lr, momentum, P, f16 ? buf->params_lowp : nullptr,
                     GE_F16, s, seg_rows > 0 ? (const float *)cws : nullptr, b_off[1], d[1], seg_rows, alpha);
 }
