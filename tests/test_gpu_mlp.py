@@ -257,6 +257,57 @@ def test_head_block_widths_lockstep(ge, hidden):
         _check_step(tr, dims, X, y, lr, mu, "f16", w0, v0, 1e-5, f"784-{hidden}-10 step {step}")
 
 
+def test_fp16_step_graph_replays_match_eager(ge):
+    """The FP16 step with the fused output layer, captured as one hipGraph of
+    three steps: under capture the weight gradients stay on the capturing
+    stream (eagerly they run on a second stream), and every replay, with
+    eager work and synchronisation between replays, lands on the eager
+    parameters bit for bit."""
+    dims = [784, 256, 256, 10]
+    B, lr, mu = 512, 0.05, 0.9
+    X, y = datagen.template_images(B, 41, fmt="f16")
+    tX, ty = torch.from_numpy(X).half().cuda(), torch.from_numpy(y).cuda()
+    p0 = torch.from_numpy(datagen.he_uniform_flat(dims)).float().cuda()
+    tr = ge.MLPTrainer(dims, B, torch.float16, params=p0)
+
+    def reset():
+        tr.params.copy_(p0)
+        tr.velocity.zero_()
+        tr.sync_lowp()
+
+    def steps():
+        for _ in range(3):
+            tr.step(tX, ty, lr, mu)
+
+    steps()  # eager: the weight gradients on the second stream
+    torch.cuda.synchronize()
+    reset()
+    steps()
+    torch.cuda.synchronize()
+    p_eager = tr.params.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps()  # the capture stream's own warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        steps()
+    for r in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tr.params, p_eager), f"replay {r}"
+        # eager work between the replays
+        reset()
+        steps()
+        torch.cuda.synchronize()
+        assert torch.equal(tr.params, p_eager), f"eager after replay {r}"
+    del graph
+
+
 def test_mlp_step_deterministic(ge):
     dims = [784, 512, 512, 10]
     X, y = datagen.template_images(1000, 9, fmt="f16")
