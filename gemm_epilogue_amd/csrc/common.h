@@ -134,7 +134,11 @@ inline bool vec_aligned(const void *p, int64_t ld, int esize, int bytes) {
 // internal launchers (validated arguments)
 // colpart (optional, 16-byte aligned): per-tile-row FP32 column sums of the
 // stored C, [gemm_colsum_rows(a) x N]; allowed when gemm_colsum_rows(a) > 0
-int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart = nullptr);
+// deferred (optional): a split-K GEMM whose epilogue is alpha times the sum
+// into row-major FP32 C skips its finishing pass, leaves splits x M x N
+// partials in the workspace (split-major) and sets *deferred to the split
+// count (0 when the result was written)
+int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart = nullptr, int *deferred = nullptr);
 int64_t gemm_colsum_rows(const ge_gemm_args &a);
 int64_t gemm_colsum_bytes(int ab_type, int64_t M, int64_t N, int64_t K);
 // out[n] = alpha * sum over r < rows of part[r][n], rows added in order
@@ -188,11 +192,18 @@ int block_fused_launch(const ge_block_fused_args &a, hipStream_t s);
 int to_lowp_launch(const float *w, int64_t n, void *w_lowp, int lowp_type, hipStream_t s);
 int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t s);
 int64_t rmsnorm_ws_bytes(int64_t rows, int64_t D);
-// seg_part (optional): g[seg_g0 .. seg_g0 + seg_len) is first set to
-// seg_alpha times the sum of seg_rows partial rows [seg_rows x seg_len] (g is
-// written only then)
+// A gradient segment the update forms first: g[g0 .. g0 + len) = alpha
+// times the sum of `rows` partial rows [rows x len], added in row order.
+struct SgdSegmentDesc {
+  const float *part;
+  int64_t g0, len;
+  int rows;
+  float alpha;
+};
+constexpr int kSgdMaxSegments = 4;
+// segs (optional, up to kSgdMaxSegments, not overlapping): the segments of g
+// formed (and written to g) before the update reads them
 int sgd_launch(float *w, float *g, float *v, float lr, float mu, int64_t n, void *wl, int lt, hipStream_t s,
-               const float *seg_part = nullptr, int64_t seg_g0 = 0, int64_t seg_len = 0, int seg_rows = 0,
-               float seg_alpha = 1.f);
+               const SgdSegmentDesc *segs = nullptr, int nseg = 0);
 
 }  // namespace ge

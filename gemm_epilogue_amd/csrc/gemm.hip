@@ -218,7 +218,8 @@ int64_t gemm_colsum_bytes(int ab_type, int64_t M, int64_t N, int64_t K) {
   return pl.splits == 1 && pl.bn < 256 ? (int64_t)pl.tiles_m * N * 4 : 0;
 }
 
-int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart) {
+int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart, int *deferred) {
+  if (deferred) *deferred = 0;
   if (a.M == 0 || a.N == 0) return GE_OK;
   Plan pl = make_plan(a.ab_type, a.M, a.N, a.K, a.split_k);
   if (colpart != nullptr && (!colsum_fusable(pl, a) || ((uintptr_t)colpart % 16) != 0)) {
@@ -302,6 +303,13 @@ int gemm_launch(const ge_gemm_args &a, hipStream_t s, float *colpart) {
   else gemm_dispatch_f32(a.layout, pl, gp, s);
   int st = launch_status("gemm_bias_act");
   if (st != GE_OK || pl.splits <= 1) return st;
+  // a plain FP32 result (alpha times the sum, row-major, nothing else in the
+  // epilogue) may leave its split partials for the caller to add
+  if (deferred && !a.bias && a.act == GE_ACT_NONE && !a.aux && !a.residual && !a.pre && a.c_type == GE_F32 &&
+      a.ldc == a.N) {
+    *deferred = pl.splits;
+    return GE_OK;
+  }
   const int64_t items = a.M * ((a.N + 3) / 4);
   if (items < (64 << 10) && pl.splits >= 8)
     hipLaunchKernelGGL(splitk_finish_wide_kernel, dim3((unsigned)((items * 8 + 255) / 256)), dim3(256), 0, s, gp);

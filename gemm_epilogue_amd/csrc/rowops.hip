@@ -453,9 +453,10 @@ int rmsnorm_launch(const ge_rmsnorm_args &a, hipStream_t st) {
 // "Capstone 5", section "Read the worked reference": one grid-stride update
 // over the flat parameter buffer: vel = mu * v - lr * g; v = vel; w += vel.
 // Four elements per thread per iteration (16-byte accesses).  Optionally the
-// gradient of one segment of the buffer is formed here first: alpha times the
-// sum of `rows` partial rows (added in row order), also written to g, so the
-// column sums that produced the partials need no launch of their own.
+// gradient of up to four segments of the buffer is formed here first: alpha
+// times the sum of `rows` partial rows (added in row order), also written to
+// g, so the column sums or split-K GEMMs that produced the partials need no
+// finishing launch of their own.
 struct SgdSegment {
   const float *part;  // [rows x len]
   int64_t g0, len;    // the segment is g[g0 .. g0 + len)
@@ -463,9 +464,17 @@ struct SgdSegment {
   float alpha;
   int vec4;  // part 16-byte aligned, g0 and len multiples of 4
 };
+struct SgdSegments {
+  SgdSegment s[kSgdMaxSegments];
+  int n;
+};
 
-__device__ __forceinline__ bool sgd_in_segment(const SgdSegment &sg, int64_t k) {
-  return sg.part != nullptr && k >= sg.g0 && k < sg.g0 + sg.len;
+// the segment holding element k, or -1
+__device__ __forceinline__ int sgd_segment_of(const SgdSegments &sg, int64_t k) {
+#pragma unroll
+  for (int j = 0; j < kSgdMaxSegments; ++j)
+    if (j < sg.n && k >= sg.s[j].g0 && k < sg.s[j].g0 + sg.s[j].len) return j;
+  return -1;
 }
 // the segment's gradient at k (also stored to g[k])
 __device__ __forceinline__ float sgd_segment_grad(float *g, const SgdSegment &sg, int64_t k) {
@@ -479,34 +488,41 @@ __device__ __forceinline__ float sgd_segment_grad(float *g, const SgdSegment &sg
 
 __global__ __launch_bounds__(256) void sgd_kernel(float *__restrict__ w, float *g, float *__restrict__ v, float lr,
                                                   float mu, int64_t n, void *__restrict__ wl, int lt, int vec,
-                                                  SgdSegment sg) {
+                                                  SgdSegments sg) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
-    const bool seg = sg.part != nullptr && i + 3 >= sg.g0 && i < sg.g0 + sg.len;
+    // a quad lies in at most one segment when every segment is vec4; else
+    // each element looks its own up
+    const int j0 = sgd_segment_of(sg, i), j3 = sgd_segment_of(sg, i + 3);
     if (vec && i + 3 < n) {
       f32x4 wv = *(f32x4 *)(w + i);
-      f32x4 gv = *(const f32x4 *)(g + i);
       f32x4 vv = *(f32x4 *)(v + i);
-      if (seg && sg.vec4 && i >= sg.g0 && i + 3 < sg.g0 + sg.len) {
+      f32x4 gv;
+      if (j0 >= 0 && j0 == j3 && sg.s[j0].vec4) {
         // the whole quad: rows of 16-byte loads, eight in flight
-        const float *pp = sg.part + (i - sg.g0);
+        const SgdSegment &sj = sg.s[j0];
+        const float *pp = sj.part + (i - sj.g0);
         f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
         int r = 0;
-        for (; r + 8 <= sg.rows; r += 8) {
+        for (; r + 8 <= sj.rows; r += 8) {
           f32x4 x[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) x[u] = *(const f32x4 *)(pp + (int64_t)(r + u) * sg.len);
+          for (int u = 0; u < 8; ++u) x[u] = *(const f32x4 *)(pp + (int64_t)(r + u) * sj.len);
 #pragma unroll
           for (int u = 0; u < 8; ++u) t += x[u];
         }
-        for (; r < sg.rows; ++r) t += *(const f32x4 *)(pp + (int64_t)r * sg.len);
+        for (; r < sj.rows; ++r) t += *(const f32x4 *)(pp + (int64_t)r * sj.len);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gv[e] = sg.alpha * t[e];
+        for (int e = 0; e < 4; ++e) gv[e] = sj.alpha * t[e];
         *(f32x4 *)(g + i) = gv;
-      } else if (seg) {
+      } else if (j0 >= 0 || j3 >= 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (sgd_in_segment(sg, i + e)) gv[e] = sgd_segment_grad(g, sg, i + e);
+        for (int e = 0; e < 4; ++e) {
+          const int j = sgd_segment_of(sg, i + e);
+          gv[e] = j >= 0 ? sgd_segment_grad(g, sg.s[j], i + e) : g[i + e];
+        }
+      } else {
+        gv = *(const f32x4 *)(g + i);
       }
       float out[4];
 #pragma unroll
@@ -521,7 +537,8 @@ __global__ __launch_bounds__(256) void sgd_kernel(float *__restrict__ w, float *
       if (wl) store4_any(wl, i, lt, true, out);
     } else {
       for (int64_t k = i; k < n && k < i + 4; ++k) {
-        const float gk = seg && sgd_in_segment(sg, k) ? sgd_segment_grad(g, sg, k) : g[k];
+        const int j = sgd_segment_of(sg, k);
+        const float gk = j >= 0 ? sgd_segment_grad(g, sg.s[j], k) : g[k];
         const float vel = mu * v[k] - lr * gk;
         v[k] = vel;
         w[k] = w[k] + vel;
@@ -532,17 +549,32 @@ __global__ __launch_bounds__(256) void sgd_kernel(float *__restrict__ w, float *
 }
 
 int sgd_launch(float *w, float *g, float *v, float lr, float mu, int64_t n, void *wl, int lt, hipStream_t st,
-               const float *seg_part, int64_t seg_g0, int64_t seg_len, int seg_rows, float seg_alpha) {
+               const SgdSegmentDesc *segs, int nseg) {
   if (n == 0) return GE_OK;
   const int vec = ((uintptr_t)w % 16 == 0) && ((uintptr_t)g % 16 == 0) && ((uintptr_t)v % 16 == 0) &&
                   (wl == nullptr || (uintptr_t)wl % 8 == 0);
   const int64_t items = (n + 3) / 4;
   const unsigned blocks = (unsigned)std::min<int64_t>((items + 255) / 256, 2048);
-  SgdSegment sg{seg_part, seg_g0, seg_len, seg_rows, seg_alpha,
-                ((uintptr_t)seg_part % 16 == 0) && seg_g0 % 4 == 0 && seg_len % 4 == 0};
-  if (seg_part != nullptr && (seg_g0 < 0 || seg_len < 0 || seg_g0 + seg_len > n)) {
-    set_error("sgd_momentum: gradient segment out of range");
+  if (nseg < 0 || nseg > kSgdMaxSegments || (nseg > 0 && segs == nullptr)) {
+    set_error("sgd_momentum: at most %d gradient segments", kSgdMaxSegments);
     return GE_E_INVALID;
+  }
+  SgdSegments sg;
+  sg.n = 0;
+  for (int j = 0; j < kSgdMaxSegments; ++j) sg.s[j] = SgdSegment{nullptr, 0, 0, 0, 1.f, 0};
+  for (int j = 0; j < nseg; ++j) {
+    const SgdSegmentDesc &d = segs[j];
+    if (d.part == nullptr || d.rows < 1 || d.g0 < 0 || d.len < 0 || d.g0 + d.len > n) {
+      set_error("sgd_momentum: gradient segment out of range");
+      return GE_E_INVALID;
+    }
+    for (int k = 0; k < sg.n; ++k)
+      if (d.g0 < sg.s[k].g0 + sg.s[k].len && sg.s[k].g0 < d.g0 + d.len) {
+        set_error("sgd_momentum: gradient segments overlap");
+        return GE_E_INVALID;
+      }
+    sg.s[sg.n++] = SgdSegment{d.part, d.g0, d.len, d.rows, d.alpha,
+                              ((uintptr_t)d.part % 16 == 0) && d.g0 % 4 == 0 && d.len % 4 == 0};
   }
   hipLaunchKernelGGL(sgd_kernel, dim3(blocks), dim3(256), 0, st, w, g, v, lr, mu, n, wl, lt, vec, sg);
   return launch_status("sgd_momentum");

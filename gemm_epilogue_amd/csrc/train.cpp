@@ -320,6 +320,12 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   int ping = 0;
   int64_t gl_rows = 0;  // > 0: the GEMM that wrote Gl left its column partials in cws
   int seg_rows = 0;     // > 0: db1 still to be formed from cws by the update
+  // gradient segments the momentum update forms from partials: db1 from the
+  // masked dgrad's column partials, and on two streams the last split-K
+  // weight gradient of each stream (its partials stay in that stream's
+  // split-K scratch until the update, which replaces the finishing pass)
+  SgdSegmentDesc segs[kSgdMaxSegments];
+  int nseg = 0;
   for (int l = nl; l >= 1; --l) {
     ge_gemm_args a = gemm_args(GE_TN, st, d[l - 1], d[l], B, hptr(l - 1), d[l - 1], Gl, d[l],
                                buf->grads + w_off[l], d[l], GE_F32);
@@ -334,7 +340,10 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
         return GE_E_LAUNCH;
       }
     }
-    RUN(gemm_launch(a, side ? s2 : s));
+    const bool defer = fork && (l == 2 || l == 1);
+    int def = 0;
+    RUN(gemm_launch(a, side ? s2 : s, nullptr, defer ? &def : nullptr));
+    if (def > 0) segs[nseg++] = SgdSegmentDesc{(const float *)a.workspace, w_off[l], d[l - 1] * d[l], def, alpha};
     const bool fused = L.head && l == nl;  // db and dH of this layer came from the head
     // the head also summed the columns of dH_{L-1}, the bias gradient of layer L-1
     if (!(L.head && l >= nl - 1)) {
@@ -378,8 +387,9 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
       return GE_E_LAUNCH;
     }
   }
+  if (seg_rows > 0) segs[nseg++] = SgdSegmentDesc{(const float *)cws, b_off[1], d[1], seg_rows, alpha};
   return sgd_launch(buf->params, buf->grads, buf->velocity, lr, momentum, P, f16 ? buf->params_lowp : nullptr,
-                    GE_F16, s, seg_rows > 0 ? (const float *)cws : nullptr, b_off[1], d[1], seg_rows, alpha);
+                    GE_F16, s, segs, nseg);
 }
 
 }  // extern "C"
