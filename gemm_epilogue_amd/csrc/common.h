@@ -38,6 +38,16 @@ __device__ __forceinline__ u32x4 raw_buffer_rsrc(const void *base) {
 // for hazards, so it opens with five wait states: the most a buffer load
 // needs after a VALU write of an SGPR it reads (the readfirstlane below) and
 // after the SALU write of M0.
+// The same with the LDS byte address given as a 32-bit value (uniform).
+__device__ __forceinline__ void lds_dma16_at(const u32x4 &rs, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane(rs[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rs[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(rs[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rs[3])};
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(so), "{m0}"(m0v)
+               : "memory");
+}
+
 __device__ __forceinline__ void lds_dma16(const u32x4 &rs, uint32_t voff, uint32_t soff, char *dst) {
   // all uniform; readfirstlane keeps them in SGPRs where the compiler would
   // otherwise leave a copy in VGPRs

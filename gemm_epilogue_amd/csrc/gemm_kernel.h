@@ -1232,15 +1232,6 @@ __device__ __forceinline__ uint32_t x8_soff(int64_t ld, int es, int k0, int ins,
   return KC ? (uint32_t)(((int64_t)r0 * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * KPI) * ld * es);
 }
 
-// One 16-byte-per-lane load of instruction ins into LDS (lane l's bytes land
-// at lds_tile + ins * 1024 + 16 l); base points at the tile's first row
-// (k-contiguous) or first column (m/n-contiguous).
-template <bool KC, int W>
-__device__ __forceinline__ void x8_load(const u32x4 &rs, int64_t ld, int es, int k0, char *lds_tile, int ins, int wv,
-                                        const uint32_t (&vo)[2]) {
-  lds_dma16(rs, vo[ins & 1], x8_soff<KC, W>(ld, es, k0, ins, wv), lds_tile + ins * 1024);
-}
-
 // The same 16 bytes for the last, partial k-tile (K % 64 != 0): an ordinary
 // load and LDS store, zero where the lane's k (its 8-wide chunk of a
 // k-contiguous row, or its k-row) is at or past K, so the padded products
@@ -1316,6 +1307,15 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
   uint32_t voa[2], vob[2];
   x8_lane_offsets<A_KC, BM>(p.lda, es, lane, mv, voa);
   x8_lane_offsets<B_KC, BN>(p.ldb, es, lane, nv, vob);
+  // the loads' LDS and scalar addresses at k-tile 0, and their step per k-tile
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)smem);
+  uint32_t soa[4], sob[BPW];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) soa[u] = x8_soff<A_KC, BM>(p.lda, es, 0, wave * 4 + u, mv);
+#pragma unroll
+  for (int u = 0; u < BPW; ++u) sob[u] = x8_soff<B_KC, BN>(p.ldb, es, 0, wave * BPW + u, nv);
+  const uint32_t dka = (uint32_t)(A_KC ? X8_BK * es : (int64_t)X8_BK * p.lda * es);
+  const uint32_t dkb = (uint32_t)(B_KC ? X8_BK * es : (int64_t)X8_BK * p.ldb * es);
   // a stage: 32 instructions for the A tile (4 per wave), BN / 8 for the B tile
   auto issue = [&](int t) {
     char *st = smem + (t % NS) * STAGE;
@@ -1328,10 +1328,17 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
         x8_load_tail<B_KC, BN>((const char *)Bb, p.ldb, es, t * X8_BK, p.K, st + TILE_A, wave * BPW + u, nv, vob, lane);
       return;
     }
+    const uint32_t sl = lds0 + (uint32_t)((t % NS) * STAGE);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x8_load<A_KC, BM>(ra, p.lda, es, t * X8_BK, st, wave * 4 + u, mv, voa);
+    for (int u = 0; u < 4; ++u) {
+      const int ins = wave * 4 + u;
+      lds_dma16_at(ra, voa[ins & 1], soa[u] + (uint32_t)t * dka, sl + ins * 1024);
+    }
 #pragma unroll
-    for (int u = 0; u < BPW; ++u) x8_load<B_KC, BN>(rb, p.ldb, es, t * X8_BK, st + TILE_A, wave * BPW + u, nv, vob);
+    for (int u = 0; u < BPW; ++u) {
+      const int ins = wave * BPW + u;
+      lds_dma16_at(rb, vob[ins & 1], sob[u] + (uint32_t)t * dkb, sl + TILE_A + ins * 1024);
+    }
   };
 
   f32x16 acc[FA][2];
