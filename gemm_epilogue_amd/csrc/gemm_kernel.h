@@ -1232,23 +1232,27 @@ __device__ __forceinline__ uint32_t x8_soff(int64_t ld, int es, int k0, int ins,
   return KC ? (uint32_t)(((int64_t)r0 * ld + k0) * es) : (uint32_t)((int64_t)(k0 + ins * KPI) * ld * es);
 }
 
-// The same 16 bytes for the last, partial k-tile (K % 64 != 0): an ordinary
-// load and LDS store, zero where the lane's k (its 8-wide chunk of a
-// k-contiguous row, or its k-row) is at or past K, so the padded products
-// add exact zeros.  The LDS slot is the lane's, as the direct load writes it.
+// The last, partial k-tile (K % 64 != 0) goes through ordinary loads and LDS
+// stores, zero where the lane's k (its 8-wide chunk of a k-contiguous row,
+// or its k-row) is at or past K, so the padded products add exact zeros; the
+// LDS slot is the lane's, as the direct load writes it.  This gives the
+// lane's byte offset from the tile base and sets ok = (k < K); a lane at or
+// past K gets an in-bounds offset of the same tile (chunk 0 of its row, or
+// k-row K - 1 of its columns), so every load is issued before any is used.
 template <bool KC, int W>
-__device__ __forceinline__ void x8_load_tail(const char *base, int64_t ld, int es, int k0, int K, char *lds_tile,
-                                             int ins, int wv, const uint32_t (&vo)[2], int lane) {
+__device__ __forceinline__ uint32_t x8_tail_off(int64_t ld, int es, int k0, int K, int ins, int wv,
+                                                const uint32_t (&vo)[2], int lane, bool &ok) {
   constexpr int KPI = 1024 / (2 * W);
-  int k;
+  const uint32_t off = vo[ins & 1] + x8_soff<KC, W>(ld, es, k0, ins, wv);
   if constexpr (KC) {
-    k = k0 + 8 * ((lane & 7) ^ x8_kc_swz((ins & 1) * 8 + (lane >> 3)));
+    const int c = (lane & 7) ^ x8_kc_swz((ins & 1) * 8 + (lane >> 3));
+    ok = k0 + 8 * c < K;
+    return ok ? off : off - (uint32_t)(8 * c * es);
   } else {
-    k = k0 + ins * KPI + (W == 256 ? (lane >> 5) : (lane >> 4));
+    const int k = k0 + ins * KPI + (W == 256 ? (lane >> 5) : (lane >> 4));
+    ok = k < K;
+    return ok ? off : off - (uint32_t)((int64_t)(k - (K - 1)) * ld * es);
   }
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (k < K) v = *(const u32x4 *)(base + vo[ins & 1] + x8_soff<KC, W>(ld, es, k0, ins, wv));
-  *(lds_u32x4 *)(lds_tile + ins * 1024 + lane * 16) = v;
 }
 
 // fragment of the 32x32x16 MFMA: rows r .. r+31 of the operand, k block kb
@@ -1320,12 +1324,22 @@ __global__ __launch_bounds__(512, 1) void gemm_x8_kernel(GemmParams p) {
   auto issue = [&](int t) {
     char *st = smem + (t % NS) * STAGE;
     if (ktail && t == nk - 1) {
+      u32x4 va[4], vb[BPW];
+      bool oa[4], ob[BPW];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        x8_load_tail<A_KC, BM>((const char *)Ab, p.lda, es, t * X8_BK, p.K, st, wave * 4 + u, mv, voa, lane);
+        va[u] = *(const u32x4 *)((const char *)Ab +
+                                 x8_tail_off<A_KC, BM>(p.lda, es, t * X8_BK, p.K, wave * 4 + u, mv, voa, lane, oa[u]));
 #pragma unroll
       for (int u = 0; u < BPW; ++u)
-        x8_load_tail<B_KC, BN>((const char *)Bb, p.ldb, es, t * X8_BK, p.K, st + TILE_A, wave * BPW + u, nv, vob, lane);
+        vb[u] = *(const u32x4 *)((const char *)Bb +
+                                 x8_tail_off<B_KC, BN>(p.ldb, es, t * X8_BK, p.K, wave * BPW + u, nv, vob, lane, ob[u]));
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *(lds_u32x4 *)(st + (wave * 4 + u) * 1024 + lane * 16) = oa[u] ? va[u] : zero;
+#pragma unroll
+      for (int u = 0; u < BPW; ++u)
+        *(lds_u32x4 *)(st + TILE_A + (wave * BPW + u) * 1024 + lane * 16) = ob[u] ? vb[u] : zero;
       return;
     }
     const uint32_t sl = lds0 + (uint32_t)((t % NS) * STAGE);
