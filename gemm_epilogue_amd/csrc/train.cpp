@@ -301,11 +301,14 @@ int mlp_train_step(const ge_mlp_desc *desc, const ge_mlp_buffers *buf, const voi
   // beside the dgrad chain and the first layer's weight gradient: each waits
   // for the event recorded when its dZ is complete, and the momentum update
   // waits for the second stream.  Both orders compute the same values; the
-  // memory-bound passes of one stream fill in beside the other's GEMMs.  Not
-  // under stream capture, where the step stays on the caller's stream.
+  // memory-bound passes of one stream fill in beside the other's GEMMs.  Only
+  // for up to three layers: with more, the dgrad chain would overwrite a dZ
+  // buffer of its ping-pong pair while a weight gradient on the second
+  // stream still reads it.  Not under stream capture, where the step stays
+  // on the caller's stream.
   hipStream_t s2 = s;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  bool fork = L.head;
+  bool fork = L.head && nl <= 3;
   if (fork) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) {

@@ -257,6 +257,34 @@ def test_head_block_widths_lockstep(ge, hidden):
         _check_step(tr, dims, X, y, lr, mu, "f16", w0, v0, 1e-5, f"784-{hidden}-10 step {step}")
 
 
+def test_fp16_four_layers_lockstep(ge):
+    """FP16 storage with three hidden layers and the fused output layer (the
+    dgrad chain reuses its dZ buffers, so this step stays on one stream), a
+    batch of 256, two steps lock-step against the oracle."""
+    dims = [784, 256, 256, 256, 10]
+    B, lr, mu = 256, 0.05, 0.9
+    p0 = datagen.he_uniform_flat(dims)
+    tr = ge.MLPTrainer(dims, B, torch.float16, params=torch.from_numpy(p0).float().cuda())
+    for step in range(2):
+        X, y = datagen.template_images(B, 43, fmt="f16", batch=step)
+        w0, v0 = host(tr.params), host(tr.velocity)
+        tr.step(torch.from_numpy(X).half().cuda(), torch.from_numpy(y).cuda(), lr, mu)
+        torch.cuda.synchronize()
+        # end to end (the dZ buffers of the first layers are overwritten by
+        # then, so no stage-wise check): loss, argmax, gradients, FP16 copy
+        ws = tr.workspace_views(B)
+        H_gpu = [host(h) for h in ws["H"]]
+        Z = host(ws["Z"])
+        e2e = oracle.mlp_step(w0, v0, dims, X, y, lr, mu, plan="f16", mask_hint=H_gpu, tie_abs=1e-5)
+        loss = host(tr.loss)[0]
+        rl = abs(loss - e2e["loss"]) / abs(e2e["loss"])
+        gc = compare(host(tr.grads), e2e["grads"], TOL_LOWP, "f32", cancel=True)
+        ok, nd = _argmax_ok(Z, e2e["Z"])
+        print(f"784-256-256-256-10 step {step}: loss rel diff {rl:.3e}, grads cos {gc['cos']:.9f}", flush=True)
+        assert rl <= TOL_LOSS and np.all(ok) and gc["cos"] > 0.99999, (step, rl, nd, gc["cos"])
+        np.testing.assert_array_equal(host(tr.params_lowp), oracle.round_fmt(host(tr.params), "f16"))
+
+
 def test_fp16_step_graph_replays_match_eager(ge):
     """The FP16 step with the fused output layer, captured as one hipGraph of
     three steps: under capture the weight gradients stay on the capturing
