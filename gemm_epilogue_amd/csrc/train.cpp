@@ -87,10 +87,10 @@ MlpLayout layout_of(const ge_mlp_desc *d, int64_t B) {
   L.gemm_ws = gws;
   off = align_up(off + gws);
   // the weight-gradient GEMMs that run beside the dgrad chain (with the fused
-  // output layer) need split-K scratch of their own
+  // output layer and up to three layers) need split-K scratch of their own
   L.head = use_head(d, B);
   L.gemm_ws2_off = off;
-  if (L.head) off = align_up(off + gws);
+  if (L.head && nl <= 3) off = align_up(off + gws);
   L.cs_ws_off = off;
   L.cs_ws = cws;
   off = align_up(off + cws);
