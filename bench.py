@@ -93,12 +93,21 @@ class Timer:
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e3  # us
 
-    def per_launch(self, fn, reps=10, n=20, warm=3):
+    def per_launch(self, fn, reps=10, n=20, warm=3, warm_ms=30.0):
         """Median and CV over `reps` measurements of `n` back-to-back launches
         each (the host enqueues faster than the kernels run, so no host time
-        enters the interval)."""
+        enters the interval).  The untimed warm-up keeps the GPU busy for at
+        least `warm_ms` first: straight after the host-side set-up of a new
+        workload the first few milliseconds of launches ran up to 8 % slower
+        (4096^3 GEMM: 128-130 us against 120 us once warm)."""
         for _ in range(warm):
             fn()
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warm_ms:
+            for _ in range(n):
+                fn()
+            self.torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
             ts.append(self.once(lambda: [fn() for _ in range(n)]) / n)
@@ -164,7 +173,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB elementwise copy, the reference dispatch for "
                          "scaling hardware byte counters (FETCH_SIZE / WRITE_SIZE) to bytes")
-    ap.add_argument("--only", choices=("gemm4096", "cfg0", "block", "gru", "bandwidth"),
+    ap.add_argument("--only", choices=("gemm4096", "cfg0", "block", "gru", "bandwidth", "blas"),
                     help="time one of the extra workloads alone and print its record (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -186,7 +195,8 @@ def main():
                 "cfg0": lambda: bench_cfg0(torch, ge, datagen, dev, tm),
                 "block": lambda: bench_block(torch, ge, datagen, dev, tm),
                 "gru": lambda: bench_gru(torch, ge, datagen, dev, tm),
-                "bandwidth": lambda: bench_bandwidth(torch, ge, datagen, dev, tm)}
+                "bandwidth": lambda: bench_bandwidth(torch, ge, datagen, dev, tm),
+                "blas": lambda: bench_blas_context(torch, ge, dev, tm)}
         print(json.dumps({"only": args.only, args.only: runs[args.only]()}), flush=True)
         return
 
@@ -297,6 +307,7 @@ def main():
         rec["mlp_784_256_10_epoch"] = fresh(lambda: bench_cfg0(torch, ge, datagen, dev, tm))
         rec["mlp_block"] = fresh(lambda: bench_block(torch, ge, datagen, dev, tm))
         rec["bandwidth_kernels"] = fresh(lambda: bench_bandwidth(torch, ge, datagen, dev, tm))
+        rec["blas_context"] = fresh(lambda: bench_blas_context(torch, ge, dev, tm))
 
     if args.copy_calibration:
         # reads 256 MiB and writes 256 MiB; run it twice so one dispatch is warm
@@ -338,6 +349,33 @@ def bench_gemm4096(torch, ge, dev, tm):
             del C
         out[layout] = r
         del A, Bm
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_blas_context(torch, ge, dev, tm):
+    """Context, not part of the path: the platform BLAS (torch.matmul) on the
+    step's forward GEMM shapes and on 4096^3, FP16 NN with an FP16 store and
+    no epilogue, beside this library's kernel on the same operands, plain and
+    with the bias + ReLU epilogue.  Median of 10 x 20 back-to-back launches."""
+    log("timing the platform BLAS for context")
+    out = {}
+    g = torch.Generator(device="cpu").manual_seed(2)
+    for (M, N, Kd) in ((4096, 2048, 2048), (4096, 2048, 784), (4096, 4096, 4096)):
+        A = (torch.randn(M, Kd, generator=g) / 64).half().to(dev)
+        Bm = (torch.randn(Kd, N, generator=g) / 64).half().to(dev)
+        bias = (torch.randn(N, generator=g) * 0.1).to(dev)
+        C = torch.empty(M, N, dtype=torch.float16, device=dev)
+        fl = 2 * M * N * Kd
+        r = {}
+        for name, fn in (("blas_matmul", lambda: torch.matmul(A, Bm, out=C)),
+                         ("ours_plain", lambda: ge.gemm_bias_act(A, Bm, "NN", out=C)),
+                         ("ours_bias_relu", lambda: ge.gemm_bias_act(A, Bm, "NN", bias=bias, act="relu", out=C))):
+            us, cv = tm.per_launch(fn)
+            r[name] = {"us": round(us, 1), "cv": round(cv, 4),
+                       "frac_of_peak": round(fl / (us * 1e-6) / 1e12 / PEAK_F16_TFLOPS, 4)}
+        out[f"{M}x{N}x{Kd}"] = r
+        del A, Bm, bias, C
     torch.cuda.empty_cache()
     return out
 
