@@ -49,7 +49,7 @@ BATCH, LR, MU, N_BATCHES = 4096, 0.05, 0.9, 50
 # is reported as null until the counters are taken again.
 TRAFFIC_BY_SOURCE = {
     # FETCH_SIZE 41,124 KiB x 2.0 + WRITE_SIZE 16,384 KiB x 1.0 per launch
-    "4f01f6f5a65915b9": 100_999_168,
+    "24210d53d961244f": 100_999_168,
 }
 
 
@@ -147,7 +147,39 @@ def cpu_baseline(seconds_target=12.0):
     return {"value": round(n / dt, 1), "unit": "samples/s", "cores": cores, "kind": "oracle",
             "cpu": cpu_model(), "host_threads": os.cpu_count(),
             "sample": f"{reps} oracle steps of batch 512 of the same 784-2048-2048-10 FP16-storage "
-                      f"workload ({n} samples, {dt:.1f} s, float64 numpy, {cores} BLAS threads)"}
+                      f"workload ({n} samples, {dt:.1f} s, float64 numpy, {cores} BLAS threads)",
+            "single_thread": cpu_single_thread()}
+
+
+def cpu_single_thread(reps=10):
+    """The oracle on one host thread for the two small workloads: one step of
+    the 784-256-10 FP32 MLP at batch 128 and one 128x256x784 FP16 GEMM with
+    bias + ReLU (median of `reps` calls each)."""
+    import threadpoolctl
+    import datagen
+    import oracle
+    dims = [784, 256, 10]
+    p = datagen.he_uniform_flat(dims)
+    v = np.zeros_like(p)
+    X, y = datagen.template_images(128, 100, fmt="f32", batch=2000)
+    rng = np.random.default_rng(3)
+    A = oracle.round_fmt(rng.standard_normal((128, 784)) / 28.0, "f16")
+    B = oracle.round_fmt(rng.standard_normal((784, 256)) / 28.0, "f16")
+    bias = oracle.round_fmt(rng.standard_normal(256) * 0.1, "f32")
+    out = {}
+    with threadpoolctl.threadpool_limits(1):
+        for name, fn in (("mlp_784_256_10_step_b128_us",
+                          lambda: oracle.mlp_step(p, v, dims, X, y, 0.05, 0.9, plan="f32")),
+                         ("gemm_128x256x784_bias_relu_us",
+                          lambda: oracle.gemm_epilogue(A, B, "NN", bias=bias, act="relu", out_fmt="f16"))):
+            ts = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                fn()
+                ts.append((time.perf_counter() - t0) * 1e6)
+            out[name] = round(float(np.median(ts)), 1)
+    out["threads"] = 1
+    return out
 
 
 def measure_clock(torch, ge, dev):
@@ -173,7 +205,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB elementwise copy, the reference dispatch for "
                          "scaling hardware byte counters (FETCH_SIZE / WRITE_SIZE) to bytes")
-    ap.add_argument("--only", choices=("gemm4096", "cfg0", "block", "gru", "bandwidth", "blas"),
+    ap.add_argument("--only", choices=("gemm4096", "gemm_small", "cfg0", "block", "gru", "bandwidth", "blas"),
                     help="time one of the extra workloads alone and print its record (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -192,6 +224,7 @@ def main():
 
     if args.only:
         runs = {"gemm4096": lambda: bench_gemm4096(torch, ge, dev, tm),
+                "gemm_small": lambda: bench_gemm_small(torch, ge, dev, tm),
                 "cfg0": lambda: bench_cfg0(torch, ge, datagen, dev, tm),
                 "block": lambda: bench_block(torch, ge, datagen, dev, tm),
                 "gru": lambda: bench_gru(torch, ge, datagen, dev, tm),
@@ -303,6 +336,7 @@ def main():
             torch.cuda.empty_cache()
             return fn()
         rec["gemm_epilogue_4096"] = fresh(lambda: bench_gemm4096(torch, ge, dev, tm))
+        rec["gemm_epilogue_128x256x784"] = fresh(lambda: bench_gemm_small(torch, ge, dev, tm))
         rec["gru_lm_step"] = fresh(lambda: bench_gru(torch, ge, datagen, dev, tm))
         rec["mlp_784_256_10_epoch"] = fresh(lambda: bench_cfg0(torch, ge, datagen, dev, tm))
         rec["mlp_block"] = fresh(lambda: bench_block(torch, ge, datagen, dev, tm))
@@ -351,6 +385,55 @@ def bench_gemm4096(torch, ge, dev, tm):
         del A, Bm
     torch.cuda.empty_cache()
     return out
+
+
+def bench_gemm_small(torch, ge, dev, tm):
+    """The small GEMM-epilogue shape, 128x256x784 (one 784-wide layer on a
+    128-row batch): A, B ~ N(0, 1/sqrt(K)) in FP16, bias + ReLU, three layouts,
+    FP16 and FP32 stores.  Latency-bound (51.4 MFLOP per launch): reported as
+    the GPU's time per launch within a captured graph, and the time per eager
+    call, each a median of 10 repetitions."""
+    log("timing the 128x256x784 GEMM epilogue")
+    out = {}
+    M, N, Kd = 128, 256, 784
+    g = torch.Generator(device="cpu").manual_seed(3)
+    for layout in ("NN", "NT", "TN"):
+        sa = (M, Kd) if layout != "TN" else (Kd, M)
+        sb = (Kd, N) if layout != "NT" else (N, Kd)
+        A = (torch.randn(sa, generator=g) / Kd ** 0.5).half().to(dev)
+        Bm = (torch.randn(sb, generator=g) / Kd ** 0.5).half().to(dev)
+        bias = (torch.randn(N, generator=g) * 0.1).to(dev)
+        r = {}
+        for store, dt in (("f16", torch.float16), ("f32", torch.float32)):
+            C = torch.empty(M, N, dtype=dt, device=dev)
+            fn = lambda: ge.gemm_bias_act(A, Bm, layout, bias=bias, act="relu", out=C)
+            # eager calls are bound by the host at this size; 20 launches
+            # captured in one graph give the GPU's own time per launch
+            eager_us, eager_cv = tm.per_launch(fn)
+            us, cv = graph_per_launch(torch, tm, fn)
+            r[store] = {"us": round(us, 2), "cv": round(cv, 4),
+                        "tflops": round(2 * M * N * Kd / (us * 1e-6) / 1e12, 2),
+                        "eager_us": round(eager_us, 2), "eager_cv": round(eager_cv, 4)}
+        out[layout] = r
+    return out
+
+
+def graph_per_launch(torch, tm, fn, n=20):
+    """Time per launch of `fn` with `n` launches captured in one graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    us, cv = tm.per_launch(g.replay, reps=10, n=5)
+    del g
+    return us / n, cv
 
 
 def bench_blas_context(torch, ge, dev, tm):
