@@ -49,7 +49,7 @@ BATCH, LR, MU, N_BATCHES = 4096, 0.05, 0.9, 50
 # is reported as null until the counters are taken again.
 TRAFFIC_BY_SOURCE = {
     # FETCH_SIZE 41,124 KiB x 2.0 + WRITE_SIZE 16,384 KiB x 1.0 per launch
-    "24210d53d961244f": 100_999_168,
+    "5515feea01e13e03": 100_999_168,
 }
 
 

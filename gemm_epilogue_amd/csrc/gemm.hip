@@ -171,10 +171,10 @@ Plan make_plan(int ab_type, int64_t M, int64_t N, int64_t K, int split_k) {
       const int64_t want = (512 + tiles - 1) / tiles;
       s = (int)std::min<int64_t>(want, pl.nk / (pl.bn == 16 ? 2 : 8));
       s = std::max(1, std::min(s, 64));
-    } else if (tiles <= 16 && pl.nk >= 8) {
-      // a handful of tiles with a short k loop waits on each k-step's loads:
-      // runs of three or four k-tiles per split, even with the finishing
-      // pass (128x256x784 FP16, eight 64x64 tiles, GPU time per launch:
+    } else if (ab_type != GE_F32 && pl.bn == 64 && tiles <= 16 && pl.nk >= 8) {
+      // a handful of 64x64 tiles with a short k loop waits on each k-step's
+      // loads: runs of three or four k-tiles per split, even with the
+      // finishing pass (128x256x784 FP16, eight tiles, GPU time per launch:
       // 12.3 / 9.5 / 14.9 us NN / NT / TN in one launch, 9.0 / 8.1 / 9.8
       // split four ways)
       s = pl.nk / 3;
