@@ -18,28 +18,27 @@ namespace ge {
 // "Capstone 5: train a network with your CUDA kernels", section "Work through
 // the backward pass": db = sum_rows(dZ), a reduction across the batch.
 //
-// A block of 256 threads owns 512 consecutive columns (eight per lane, one
-// 16-byte load for 16-bit data) and a contiguous range of rows; wave w sums
-// rows w, w+4, w+8, ... of the range in row order, keeping four rows' loads
-// in flight, then the four wave partials are added in wave order.  With
-// several row ranges the partials go to a workspace and colsum_final adds
-// them: wave w of a final block takes ranges w, w+4, ... in order and the
-// four wave sums are again added in wave order.
-constexpr int CS_VEC = 8;
-constexpr int CS_COLS = 64 * CS_VEC;
-constexpr int CS_ROWS_MIN = 32;
-constexpr int CS_UNROLL = 4;
+// A block of 256 threads owns a strip of 256 bytes of every row (64 FP32 or
+// 128 16-bit columns: 16 lanes of 16 bytes) and a contiguous range of rows,
+// read in batches of 256 rows: lane l of wave w takes, for u = 0..15, row
+// 16 u + 4 w + l / 16 of the batch, so each wave has all sixteen of its
+// 16-byte loads in flight at once.  A lane adds its rows in order (u, then
+// batch); the four lanes of a column within a wave are added pairwise
+// ((g0 + g1) + (g2 + g3), the same value in every lane as addition commutes),
+// then the four waves in wave order.  With several row ranges the partials go
+// to a workspace and colsum_final adds them: wave w of a final block takes
+// ranges w, w+4, ... in order and the four wave sums are again added in wave
+// order.
+constexpr int CS_BATCH = 256;  // rows per block batch
+constexpr int CS_U = 16;       // loads in flight per lane
 
-template <typename T>
-__device__ __forceinline__ void cs_load8(const T *__restrict__ X, int64_t i, bool full, int left, float v[8]) {
+template <typename T, int VEC>
+__device__ __forceinline__ void cs_load(const T *__restrict__ X, int64_t i, bool full, int left, float (&v)[VEC]) {
   if (full) {
     if constexpr (sizeof(T) == 4) {
-      const f32x4 a = *(const f32x4 *)(X + i), b = *(const f32x4 *)(X + i + 4);
+      const f32x4 a = *(const f32x4 *)(X + i);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[j] = a[j];
-        v[4 + j] = b[j];
-      }
+      for (int j = 0; j < 4; ++j) v[j] = a[j];
     } else {
       typedef T T8 __attribute__((ext_vector_type(8)));
       const T8 x = *(const T8 *)(X + i);
@@ -48,7 +47,7 @@ __device__ __forceinline__ void cs_load8(const T *__restrict__ X, int64_t i, boo
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = j < left ? (float)X[i + j] : 0.f;
+    for (int j = 0; j < VEC; ++j) v[j] = j < left ? (float)X[i + j] : 0.f;
   }
 }
 
@@ -56,42 +55,54 @@ template <typename T>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const T *__restrict__ X, int M, int N, int64_t ldx,
                                                              int vec, int rows_per, float alpha,
                                                              float *__restrict__ out, int accumulate) {
-  __shared__ float red[3][CS_COLS];
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int CW = 16 * VEC;  // columns per block
+  __shared__ float red[3][CW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = blockIdx.x * CS_COLS + lane * CS_VEC;
+  const int cl = lane & 15, rg = lane >> 4;
+  const int n = blockIdx.x * CW + cl * VEC;
   const int r0 = blockIdx.y * rows_per;
   const int r1 = min(M, r0 + rows_per);
-  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float s[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) s[j] = 0.f;
   if (n < N) {
-    const bool full = vec && n + CS_VEC <= N;
+    const bool full = vec && n + VEC <= N;
     const int left = N - n;
-    int r = r0 + wave;
-    for (; r + 4 * (CS_UNROLL - 1) < r1; r += 4 * CS_UNROLL) {
-      float v[CS_UNROLL][8];
+    for (int rb = r0; rb < r1; rb += CS_BATCH) {
+      float v[CS_U][VEC];
 #pragma unroll
-      for (int u = 0; u < CS_UNROLL; ++u) cs_load8(X, (int64_t)(r + 4 * u) * ldx + n, full, left, v[u]);
+      for (int u = 0; u < CS_U; ++u) {
+        const int r = rb + 16 * u + 4 * wave + rg;
+        if (r < r1) {
+          cs_load<T, VEC>(X, (int64_t)r * ldx + n, full, left, v[u]);
+        } else {
 #pragma unroll
-      for (int u = 0; u < CS_UNROLL; ++u)
+          for (int j = 0; j < VEC; ++j) v[u][j] = 0.f;
+        }
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s[j] += v[u][j];
-    }
-    for (; r < r1; r += 4) {
-      float v[8];
-      cs_load8(X, (int64_t)r * ldx + n, full, left, v);
+      for (int u = 0; u < CS_U; ++u)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] += v[j];
+        for (int j = 0; j < VEC; ++j) s[j] += v[u][j];
     }
   }
-  if (wave > 0) {
+  // the four row groups of the wave: (g0 + g1) + (g2 + g3)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) red[wave - 1][lane * CS_VEC + j] = s[j];
+  for (int j = 0; j < VEC; ++j) {
+    s[j] += __shfl_xor(s[j], 16, 64);
+    s[j] += __shfl_xor(s[j], 32, 64);
+  }
+  if (wave > 0 && rg == 0) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) red[wave - 1][cl * VEC + j] = s[j];
   }
   __syncthreads();
-  if (wave == 0 && n < N) {
+  if (wave == 0 && rg == 0 && n < N) {
     float *dst = out + (int64_t)blockIdx.y * N;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = lane * CS_VEC + j;
+    for (int j = 0; j < VEC; ++j) {
+      const int c = cl * VEC + j;
       const float t = ((s[j] + red[0][c]) + red[1][c]) + red[2][c];
       if (n + j < N) dst[n + j] = accumulate ? dst[n + j] + alpha * t : alpha * t;
     }
@@ -126,10 +137,11 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restri
 namespace {
 int colsum_splits(int64_t M, int64_t N) {
   if (M < 1024) return 1;  // one pass: a block reads all rows of its columns
-  const int64_t colblocks = (N + CS_COLS - 1) / CS_COLS;
-  int64_t want = (1024 + colblocks - 1) / colblocks;
-  int64_t maxs = std::max<int64_t>(1, M / CS_ROWS_MIN);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(maxs, 1024)));
+  // about 2048 strips of 64 columns x 256 rows, at most 64 ranges (the
+  // final pass adds them per column); independent of the element type
+  const int64_t units = (N + 63) / 64;
+  const int64_t want = (2048 + units - 1) / units;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, (M + CS_BATCH - 1) / CS_BATCH, 64}));
 }
 
 template <typename T>
@@ -164,7 +176,7 @@ int colsum_launch(const void *X, int64_t M, int64_t N, int64_t ldx, int xt, floa
                   void *ws, int64_t ws_bytes, hipStream_t st, int accumulate) {
   if (N == 0) return GE_OK;
   const int vec = vec_aligned(X, ldx, dtype_size(xt), 16);
-  const int colblocks = (int)((N + CS_COLS - 1) / CS_COLS);
+  const int colblocks = (int)((N * dtype_size(xt) + 255) / 256);
   const int splits = M > 0 ? colsum_splits(M, N) : 1;
   if (splits == 1) {
     colsum_partial_any(xt, dim3(colblocks, 1), st, X, (int)M, (int)N, ldx, vec, (int)std::max<int64_t>(M, 1),
