@@ -116,15 +116,15 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restri
   const int n = blockIdx.x * 64 + lane;
   float s = 0.f;
   if (n < N) {
-    int k = wave;
-    for (; k + 4 * 7 < splits; k += 4 * 8) {
+    // eight ranges' loads in flight, added in range order
+    for (int k = wave; k < splits; k += 4 * 8) {
       float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(k + 4 * u) * N + n];
+      for (int u = 0; u < 8; ++u) v[u] = k + 4 * u < splits ? part[(int64_t)(k + 4 * u) * N + n] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 8; ++u)
+        if (k + 4 * u < splits) s += v[u];
     }
-    for (; k < splits; k += 4) s += part[(int64_t)k * N + n];
   }
   if (wave > 0) red[wave - 1][lane] = s;
   __syncthreads();
