@@ -30,7 +30,7 @@ def host(t):
 
 @pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 1), (128, 10), (128, 256), (4096, 10), (5000, 1003), (4096, 4096),
-                                   (8192, 3072)])
+                                   (8192, 3072), (3000, 4100), (1024, 8200)])
 def test_colsum(ge, fmt, shape):
     X = datagen.normal(shape, 1.0, seed=shape[0] + shape[1], fmt=fmt)
     out = ge.colsum(dev(X, fmt), 0.25)
@@ -38,8 +38,9 @@ def test_colsum(ge, fmt, shape):
                   f"colsum {shape} {fmt}", cancel=True)
 
 
-def test_colsum_deterministic(ge):
-    X = dev(datagen.normal((10000, 777), 1.0, seed=5), "f32")
+@pytest.mark.parametrize("shape", [(10000, 777), (3000, 8200)])
+def test_colsum_deterministic(ge, shape):
+    X = dev(datagen.normal(shape, 1.0, seed=5), "f32")
     a, b = ge.colsum(X), ge.colsum(X)
     assert torch.equal(a, b)
 
@@ -132,7 +133,7 @@ def test_sgd_momentum(ge, pins, n, lowp):
 
 
 @pytest.mark.parametrize("fmt", ["f32", "f16"])
-@pytest.mark.parametrize("shape", [(100, 37), (5000, 1003), (4096, 4096)])
+@pytest.mark.parametrize("shape", [(100, 37), (5000, 1003), (4096, 4096), (3000, 8200)])
 def test_colsum_accumulate(ge, fmt, shape):
     """accumulate adds the column sums to what out holds (both the one-pass
     and the two-pass reduction)."""
