@@ -162,10 +162,7 @@ def cpu_single_thread(reps=10):
     p = datagen.he_uniform_flat(dims)
     v = np.zeros_like(p)
     X, y = datagen.template_images(128, 100, fmt="f32", batch=2000)
-    rng = np.random.default_rng(3)
-    A = oracle.round_fmt(rng.standard_normal((128, 784)) / 28.0, "f16")
-    B = oracle.round_fmt(rng.standard_normal((784, 256)) / 28.0, "f16")
-    bias = oracle.round_fmt(rng.standard_normal(256) * 0.1, "f32")
+    A, B, bias = datagen.gemm_operands(128, 256, 784, "NN", seed=3)
     out = {}
     with threadpoolctl.threadpool_limits(1):
         for name, fn in (("mlp_784_256_10_step_b128_us",
