@@ -333,11 +333,13 @@ def main():
             torch.cuda.empty_cache()
             return fn()
         rec["gemm_epilogue_4096"] = fresh(lambda: bench_gemm4096(torch, ge, dev, tm))
-        rec["gemm_epilogue_128x256x784"] = fresh(lambda: bench_gemm_small(torch, ge, dev, tm))
         rec["gru_lm_step"] = fresh(lambda: bench_gru(torch, ge, datagen, dev, tm))
         rec["mlp_784_256_10_epoch"] = fresh(lambda: bench_cfg0(torch, ge, datagen, dev, tm))
         rec["mlp_block"] = fresh(lambda: bench_block(torch, ge, datagen, dev, tm))
         rec["bandwidth_kernels"] = fresh(lambda: bench_bandwidth(torch, ge, datagen, dev, tm))
+        # after the others: timed right before the GRU step it left that
+        # step's memory-bound kernels slower (4.4 against 3.7 ms)
+        rec["gemm_epilogue_128x256x784"] = fresh(lambda: bench_gemm_small(torch, ge, dev, tm))
         rec["blas_context"] = fresh(lambda: bench_blas_context(torch, ge, dev, tm))
 
     if args.copy_calibration:
