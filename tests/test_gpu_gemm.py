@@ -251,3 +251,44 @@ def test_gemm_x8_epilogue_variants(ge, act):
                            residual=None if res is None else dev(res, fmt), pre=pre, out_dtype=TD[fmt])
     assert_parity(host(out), ref, TOL_LOWP, fmt, f"x8 {act} C", cancel=True)
     assert_parity(host(pre), pre_ref, TOL_LOWP, fmt, f"x8 {act} pre", cancel=True)
+
+
+# ------------------------------------------- launches captured in a graph --
+
+@pytest.mark.parametrize("shape,layout", [((128, 256, 784), "NN"), ((128, 256, 784), "TN"),
+                                          ((4096, 16, 2048), "NN"), ((512, 512, 512), "NT")],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_gemm_graph_replays_match_eager(ge, shape, layout):
+    """gemm_bias_act captured in a graph (split-K with its finishing pass for
+    the short-k and narrow shapes, one launch for the last): every replay,
+    with eager work between them, gives the eager result bit for bit."""
+    M, N, K = shape
+    print(f"graph gemm {layout} {M}x{N}x{K}", flush=True)
+    A, B, bias = datagen.gemm_operands(M, N, K, layout, seed=9)
+    tA, tB, tb = dev(A, "f16"), dev(B, "f16"), dev(bias, "f32")
+    ws = torch.empty(max(1, ge.gemm_workspace_bytes(layout, torch.float16, M, N, K)), dtype=torch.uint8,
+                     device="cuda")
+    C = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    ge.gemm_bias_act(tA, tB, layout, bias=tb, act="relu", out=C, workspace=ws)
+    torch.cuda.synchronize()
+    ref = C.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ge.gemm_bias_act(tA, tB, layout, bias=tb, act="relu", out=C, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ge.gemm_bias_act(tA, tB, layout, bias=tb, act="relu", out=C, workspace=ws)
+    for i in range(3):
+        C.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, ref), f"replay {i}"
+        # eager work between the replays, on the same buffers
+        ge.gemm_bias_act(tA, tB, layout, bias=tb, act="none", out=C, workspace=ws)
+        torch.cuda.synchronize()
+    assert_parity(host(ref), oracle.gemm_epilogue(A, B, layout, 1.0, bias, "relu", out_fmt="f16")[0], TOL_LOWP,
+                  "f16", f"graph {layout} {M}x{N}x{K}", cancel=True)
