@@ -353,21 +353,27 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(ge_rmsnorm_args a, int vx,
   const int row = blockIdx.x * 4 + wave;
   const bool live = row < a.rows;
   const int D = (int)a.D;
-  float xh[CH][4], g[CH][4];
+  float xh[CH][4], g[CH][4], rs[CH][4];
   float dot = 0.f;
   const float r = live ? a.r[row] : 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int j = (c * 64 + lane) * 4;
     float xv[4], dv[4];
+    // the residual gradient is read with x and dy, so the row's reads all
+    // go out before the reduction
     if (live && j + 3 < D) {
       load4_any(a.x, row * a.ld_x + j, a.x_type, vx, xv);
       load4_any(a.dy, row * a.ld_dy + j, a.dy_type, vdy, dv);
+      if (a.dres) load4_any(a.dres, row * a.ld_dres + j, a.dres_type, vres, rs[c]);
+      else
+        for (int e = 0; e < 4; ++e) rs[c][e] = 0.f;
     } else {
       for (int e = 0; e < 4; ++e) {
         const bool ok = live && j + e < D;
         xv[e] = ok ? load_any(a.x, row * a.ld_x + j + e, a.x_type) : 0.f;
         dv[e] = ok ? load_any(a.dy, row * a.ld_dy + j + e, a.dy_type) : 0.f;
+        rs[c][e] = ok && a.dres ? load_any(a.dres, row * a.ld_dres + j + e, a.dres_type) : 0.f;
       }
     }
 #pragma unroll
@@ -385,14 +391,9 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(ge_rmsnorm_args a, int vx,
     for (int c = 0; c < CH; ++c) {
       const int j = (c * 64 + lane) * 4;
       if (j >= D) continue;
-      float dx[4], rs[4] = {0.f, 0.f, 0.f, 0.f};
-      if (a.dres) {
-        if (j + 3 < D) load4_any(a.dres, row * a.ld_dres + j, a.dres_type, vres, rs);
-        else
-          for (int e = 0; e < 4; ++e) rs[e] = (j + e < D) ? load_any(a.dres, row * a.ld_dres + j + e, a.dres_type) : 0.f;
-      }
+      float dx[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dx[e] = r * (g[c][e] - xh[c][e] * cm) + rs[e];
+      for (int e = 0; e < 4; ++e) dx[e] = r * (g[c][e] - xh[c][e] * cm) + rs[c][e];
       if (j + 3 < D) {
         store4_any(a.dx, row * a.ld_dx + j, a.dx_type, vdx, dx);
       } else {
